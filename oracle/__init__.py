@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for exact attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library.
+"""
+
+from .attention import (  # noqa: F401
+    allowed_mask,
+    attention_decode,
+    attention_dense,
+    attention_flops,
+    attention_varlen,
+    merge_states,
+    online_attention,
+    sdpa,
+)
