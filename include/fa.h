@@ -1,0 +1,129 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) attention forward library, libfa.so.
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T) V,   softmax over each row of the scores,
+ * with causal and sliding-window masks, and also returns the per-row
+ * log-sum-exp lse_i = ln sum_{allowed j} exp(scale * q_i . k_j).
+ * The definition is the SDPA equation of "FlashAttention" (aiwiki.page),
+ * section "Attention and the memory bottleneck"; the row statistics that make
+ * the tiled evaluation exact are the update equations of its section "Tiling
+ * and online normalisation"; lse is the compact normalisation information of
+ * its section "Training and computational complexity".  The interfaces
+ * offered (multi-head, causal and sliding-window masks, variable-length
+ * sequences, inference against cached keys/values) are the ones listed in its
+ * section "Software integration and limitations".
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers; the caller allocates and owns
+ *    every buffer (including the decode workspace).  The library allocates
+ *    nothing and keeps no global state; calls are thread-safe.
+ *  - Tensors are contiguous, row-major, in the layouts stated per call.
+ *    q, k, v, o and the workspace must be 16-byte aligned; lse 4-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Each call only
+ *    enqueues kernels on it and returns; it never synchronises.
+ *  - Errors are returned as fa_status codes, never by abort.  Arguments are
+ *    checked on the host before anything is launched.  Lengths held in device
+ *    arrays (cu_seqlens_*, seqlens_k) cannot be checked without a sync: their
+ *    validity is a precondition (stated per call); the kernels clamp every
+ *    read to the buffer sizes implied by the other arguments.
+ *  - There is no fallback path: an unsupported combination returns
+ *    FA_ERR_UNSUPPORTED instead of running something slower.
+ *  - Masks (all positions 0-based within one sequence, delta = n_k - n_q):
+ *      causal:        key j allowed for query i iff j <= i + delta
+ *                     (bottom-right aligned);
+ *      window_left W: key j allowed iff j >= i + delta - W  (W < 0: none);
+ *    with both, a row sees at most W + 1 keys.  A row with no allowed key
+ *    gets O = 0 and lse = -inf.
+ *  - Arithmetic: bf16 inputs are multiplied on matrix cores with fp32
+ *    accumulation; the softmax runs in fp32 in base 2 with log2(e) folded into
+ *    the scale; the probabilities are rounded to bf16 (RNE) before the P V
+ *    product; O is rounded to the output type once, at the end.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, scale not finite > 0 */
+  FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: head dim, chunk size, varlen+fp32 */
+  FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required */
+  FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward (prefill), bf16 in, bf16 out.
+ *
+ * Dense (cu_seqlens_q == cu_seqlens_k == NULL):
+ *   q, o: [batch, seqlen_q, heads, d] bf16;  k, v: [batch, seqlen_k, heads, d] bf16;
+ *   lse:  [batch, heads, seqlen_q] fp32, or NULL if not wanted.
+ * Varlen (both cu_seqlens non-NULL): `batch` sequences packed along the rows;
+ *   q, o: [total_q, heads, d];  k, v: [total_k, heads, d];
+ *   lse:  [heads, total_q] fp32 or NULL;
+ *   cu_seqlens_q/k: device int32 [batch + 1], cu[0] = 0, non-decreasing;
+ *   sequence s owns rows cu[s] .. cu[s+1]-1; total_q = cu_seqlens_q[batch].
+ *   seqlen_q / seqlen_k are then the maximum per-sequence lengths (they size
+ *   the launch grid; every per-sequence length must be <= them).
+ * d: head dim, 64 or 128.  scale: finite and > 0 (usually 1/sqrt(d)).
+ * causal: 0 or 1.  window_left: < 0 for no window.
+ * batch, heads or seqlen_q == 0 is a valid no-op; seqlen_k == 0 gives
+ * O = 0, lse = -inf for every row.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int batch, int heads, int seqlen_q, int seqlen_k, int d,
+           float scale, int causal, int window_left,
+           const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream);
+
+/*
+ * fa_fwd_fp32 -- the same operation and argument list with fp32 q, k, v, o
+ * (products and accumulation in fp32 on matrix cores, softmax in fp32).
+ * Dense only: varlen returns FA_ERR_UNSUPPORTED.  d: 64 or 128.
+ */
+int fa_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse,
+                int batch, int heads, int seqlen_q, int seqlen_k, int d,
+                float scale, int causal, int window_left,
+                const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream);
+
+/*
+ * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
+ * per (batch, head, chunk) an fp32 partial output of d values and one fp32
+ * partial log-sum-exp, chunks = ceil(max_len / chunk).  Returns 0 for
+ * invalid sizes.
+ */
+size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int chunk);
+
+/*
+ * fa_decode -- one new query token per sequence against a KV cache
+ * (inference with cached keys and values; the cache already holds the
+ * current token, so every one of the sequence's cached keys is allowed).
+ *   q, o:             [batch, 1, heads, d] bf16;
+ *   k_cache, v_cache: [batch, max_len, heads, d] bf16;
+ *   seqlens_k:        device int32 [batch]; precondition 0 <= L_b <= max_len.
+ *                     Rows L_b .. max_len-1 of the cache are never read.
+ *   lse:              [batch, heads] fp32 or NULL.
+ * The keys of each sequence are split into chunks of `chunk` keys (64, 128,
+ * 256 or 512); a first kernel computes each chunk's normalised partial
+ * output and log-sum-exp into `workspace`, a second merges the chunks with
+ * log-sum-exp weights (the rescale of the online-softmax update applied to
+ * whole chunk states).  d: 64 or 128.  workspace_bytes must be at least
+ * fa_decode_workspace_size(batch, heads, max_len, d, chunk).
+ * L_b == 0 gives O = 0 and lse = -inf for that sequence.
+ */
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
+              void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
+              int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,135 @@
+// C ABI of libfa.so: argument checks, then launches on the caller's stream.
+// Every check runs on the host before any HIP call, so a rejected call has
+// touched neither the device nor the stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, float* lse,
+               int batch, int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
+               int window_left, const int* cu_q, const int* cu_k, void* stream) {
+  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
+  if (d <= 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (fp32 && cu_q != nullptr) return FA_ERR_UNSUPPORTED;
+  if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;  // nothing to compute
+  if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  // with no keys at all (seqlen_k == 0, dense) k and v are never read and may be NULL
+  if ((k == nullptr || v == nullptr) && !(seqlen_k == 0 && cu_q == nullptr))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if (cu_q != nullptr && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return FA_ERR_INVALID_ARG;
+  // the grid has batch * heads * ceil(seqlen_q / 128) workgroups
+  const long long grid = (long long)batch * heads * ((seqlen_q + 127) / 128);
+  if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.batch = batch;
+  a.heads = heads;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fp32 ? fa::launch_fwd_fp32(a, d, s) : fa::launch_fwd_bf16(a, d, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int heads,
+           int seqlen_q, int seqlen_k, int d, float scale, int causal, int window_left,
+           const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream) {
+  return fwd_common(false, q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, d, scale, causal,
+                    window_left, cu_seqlens_q, cu_seqlens_k, stream);
+}
+
+int fa_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
+                int window_left, const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream) {
+  return fwd_common(true, q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, d, scale, causal,
+                    window_left, cu_seqlens_q, cu_seqlens_k, stream);
+}
+
+size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int chunk) {
+  if (batch <= 0 || heads <= 0 || max_len <= 0 || d <= 0 || chunk <= 0) return 0;
+  const int max_chunks = (max_len + chunk - 1) / chunk;
+  const size_t lse_off = fa::decode_ws_lse_offset(batch, heads, max_chunks, d);
+  return lse_off + (size_t)batch * heads * max_chunks * sizeof(float);
+}
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
+              void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
+              int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || heads < 0 || max_len < 0 || d <= 0 || chunk <= 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (chunk != 64 && chunk != 128 && chunk != 256 && chunk != 512) return FA_ERR_UNSUPPORTED;
+  if (batch == 0 || heads == 0) return FA_OK;
+  if (max_len == 0) return FA_ERR_INVALID_ARG;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || seqlens_k == nullptr ||
+      o == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(seqlens_k, 4))
+    return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_decode_workspace_size(batch, heads, max_len, d, chunk);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return FA_ERR_WORKSPACE;
+  const int max_chunks = (max_len + chunk - 1) / chunk;
+  if ((long long)batch * heads * max_chunks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+
+  fa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      fa::decode_ws_lse_offset(batch, heads, max_chunks, d));
+  a.batch = batch;
+  a.heads = heads;
+  a.max_len = max_len;
+  a.max_chunks = max_chunks;
+  a.chunk = chunk;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_decode(a, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: combination not built";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown fa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int batch;
+  int heads;
+  int seqlen_q;  // dense: length; varlen: maximum length (grid sizing)
+  int seqlen_k;
+  float scale_log2;  // scale * log2(e): scores are kept in base 2
+  int causal;
+  int window_left;
+  const int* cu_q;  // varlen offsets, NULL for dense
+  const int* cu_k;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* seqlens;
+  void* o;
+  float* lse;
+  float* ws_o;    // [batch, heads, max_chunks, d] fp32 normalised chunk outputs
+  float* ws_lse;  // [batch, heads, max_chunks] fp32 chunk log2-sum-exp2
+  int batch;
+  int heads;
+  int max_len;
+  int max_chunks;
+  int chunk;
+  float scale_log2;
+};
+
+// Byte offset of the chunk lse array inside the decode workspace.
+inline size_t decode_ws_lse_offset(int batch, int heads, int max_chunks, int d) {
+  const size_t o_bytes = (size_t)batch * heads * max_chunks * d * sizeof(float);
+  return (o_bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,262 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64
+oracle on the same seeded inputs, element by element.
+
+Small shapes span several 128-row query tiles and 64-key K/V tiles with
+ragged tails; the five workloads run at full size in the launch configuration
+the bench times, checked on every output (2k prefill), on sampled rows of
+every head (8000-token prompt), on sampled heads of every sequence (packed
+batch) and on sampled (sequence, head) pairs (decode).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_19_amd as fa
+import oracle
+from io_aware_exact_19_amd import configs, inputs
+from tests.parity import announce, check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    return t.float().double().numpy() if t.dtype == torch.bfloat16 else t.double().numpy()
+
+
+def _dense_case(B, H, nq, nk, d, causal, W, dtype, seed, q_mult=1.0, scale=None):
+    q, k, v = inputs.dense_qkv(B, nq, nk, H, d, seed, dtype, q_mult)
+    s = 1.0 / math.sqrt(d) if scale is None else scale
+    what = f"dense B{B} H{H} nq{nq} nk{nk} d{d} causal{int(causal)} W{W} {dtype} x{q_mult}"
+    announce(what)
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), scale=s, causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_dense(_np(q), _np(k), _np(v), s, causal, W)
+    check(o.cpu(), lse.cpu(), o_ref, lse_ref, dtype, what)
+    return o.cpu(), lse.cpu(), o_ref, lse_ref
+
+
+SMALL_BF16 = [
+    # B, H, nq, nk, d, causal, window
+    (1, 2, 300, 300, 128, False, -1),
+    (2, 3, 300, 300, 128, True, -1),
+    (1, 2, 517, 517, 64, True, 100),
+    (1, 2, 200, 333, 128, True, -1),   # n_q < n_k: bottom-right causal
+    (1, 2, 333, 200, 64, True, -1),    # n_q > n_k: the first 133 rows see no key
+    (1, 1, 1, 1, 128, False, -1),
+    (1, 2, 63, 63, 128, True, -1),
+    (1, 2, 65, 65, 64, False, -1),
+    (1, 2, 200, 200, 128, True, 0),    # window 0: O = V
+    (1, 2, 200, 200, 64, True, 500),   # window wider than the sequence
+    (1, 2, 130, 130, 128, False, 7),   # window without causal
+    (3, 1, 129, 64, 64, False, -1),
+    (1, 2, 1, 700, 128, True, -1),     # one query at the end of 700 keys
+]
+
+
+@pytest.mark.parametrize("B,H,nq,nk,d,causal,W", SMALL_BF16)
+def test_dense_bf16_small(B, H, nq, nk, d, causal, W):
+    _dense_case(B, H, nq, nk, d, causal, W, torch.bfloat16, seed=1000 + nq + nk + d + W)
+
+
+def test_dense_bf16_peaked():
+    """Q multiplied by 4: peaked softmax rows."""
+    _dense_case(2, 2, 256, 256, 128, False, -1, torch.bfloat16, seed=7, q_mult=4.0)
+    _dense_case(1, 2, 300, 300, 64, True, -1, torch.bfloat16, seed=8, q_mult=4.0)
+
+
+def test_window_zero_returns_v_exactly():
+    """Causal with window 0: each row sees only its own key, so O = V bit for
+    bit (p = 1) and lse = scale * q.k."""
+    o, lse, o_ref, _ = _dense_case(1, 2, 150, 150, 128, True, 0, torch.bfloat16, seed=9)
+    _, _, v = inputs.dense_qkv(1, 150, 150, 2, 128, 9, torch.bfloat16)
+    assert torch.equal(o, v)
+
+
+def test_rows_without_keys_are_zero():
+    o, lse, o_ref, lse_ref = _dense_case(1, 2, 333, 200, 64, True, -1, torch.bfloat16, seed=10)
+    assert torch.all(o[:, :133] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, :133]))
+
+
+def test_no_keys_at_all():
+    q = inputs.normal((2, 5, 3, 64), 1).cuda()
+    k = torch.empty((2, 0, 3, 64), dtype=torch.bfloat16, device="cuda")
+    announce("dense seqlen_k=0")
+    o, lse = fa.attention(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("B,H,nq,nk,d,causal,W", [
+    (1, 2, 300, 300, 128, True, -1),
+    (1, 1, 100, 37, 64, True, 5),
+    (2, 2, 130, 130, 64, False, -1),
+])
+def test_dense_fp32_small(B, H, nq, nk, d, causal, W):
+    _dense_case(B, H, nq, nk, d, causal, W, torch.float32, seed=2000 + nq + nk)
+
+
+def test_workload_small_fp32():
+    c = configs.SMALL_FP32
+    _dense_case(c["batch"], c["heads"], c["seqlen"], c["seqlen"], c["d"], c["causal"],
+                c["window_left"], torch.float32, c["seed"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("q_mult", [1.0, 4.0])
+def test_workload_prefill_2k(causal, q_mult):
+    """B4 H16 N2048 d128 bf16, every output checked."""
+    c = configs.PREFILL_2K
+    _dense_case(c["batch"], c["heads"], c["seqlen"], c["seqlen"], c["d"], causal, -1,
+                torch.bfloat16, c["seed"], q_mult=q_mult)
+
+
+def test_workload_long_8k():
+    """B1 H32 N8000 causal d128: sampled rows (every tile boundary near the
+    start, the middle and the 64-row tail tile) of every head."""
+    c = configs.LONG_8K
+    N, H, d = c["seqlen"], c["heads"], c["d"]
+    q, k, v = inputs.dense_qkv(1, N, N, H, d, c["seed"])
+    s = configs.default_scale(d)
+    announce("long 8k causal")
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), scale=s, causal=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 1, 2, 63, 64, 127, 128, 129, 3999, 4000, 7871, 7872, 7935, 7936,
+                       7937, 7990, 7998, 7999] + list(rng.integers(0, N, 24))))
+    rows = np.array(rows)
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    o_ref = np.zeros((len(rows), H, d))
+    lse_ref = np.zeros((H, len(rows)))
+    for h in range(H):
+        o_ref[:, h], lse_ref[h] = oracle.sdpa(qn[0, rows, h], kn[0, :, h], vn[0, :, h], s, True,
+                                             q_index=rows, n_q=N)
+    check(o[0, rows], lse[0][:, rows], o_ref, lse_ref, torch.bfloat16, "long 8k sampled rows")
+
+
+def _varlen_case(lens, H, d, causal, W, seed, heads_checked=None):
+    lens = torch.as_tensor(lens)
+    cu = inputs.cu_seqlens(lens)
+    q, k, v = inputs.varlen_qkv(lens, H, d, seed)
+    s = configs.default_scale(d)
+    what = f"varlen nseq{len(lens)} H{H} d{d} causal{int(causal)} W{W}"
+    announce(what)
+    cu_d = cu.cuda()
+    o, lse = fa.attention_varlen(q.cuda(), k.cuda(), v.cuda(), cu_d, cu_d, int(lens.max()),
+                                 int(lens.max()), scale=s, causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    hs = list(range(H)) if heads_checked is None else heads_checked
+    qn, kn, vn = _np(q[:, hs]), _np(k[:, hs]), _np(v[:, hs])
+    o_ref, lse_ref = oracle.attention_varlen(qn, kn, vn, cu.numpy(), cu.numpy(), s, causal, W)
+    check(o[:, hs], lse[hs], o_ref, lse_ref, torch.bfloat16, what)
+    return q, k, v, cu, o, lse
+
+
+def test_varlen_small():
+    _varlen_case([5, 1, 300, 129, 64, 0, 200], 2, 64, True, 50, seed=31)
+    _varlen_case([130, 70, 257], 3, 128, False, -1, seed=32)
+    _varlen_case([1000, 17, 513], 2, 128, True, -1, seed=33)
+
+
+def test_varlen_equals_per_sequence_dense():
+    """The packed call and one dense call per sequence run the same tiles in
+    the same order: identical bits."""
+    lens = [300, 129, 1, 450]
+    q, k, v, cu, o, lse = _varlen_case(lens, 2, 64, True, 100, seed=34)
+    for i, n in enumerate(lens):
+        a, b = int(cu[i]), int(cu[i + 1])
+        od, ld = fa.attention(q[None, a:b].cuda(), k[None, a:b].cuda(), v[None, a:b].cuda(),
+                              causal=True, window_left=100)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0].cpu(), o[a:b])
+        assert torch.equal(ld[0].cpu(), lse[:, a:b])
+
+
+def test_workload_varlen():
+    """16 sequences, lengths U[128, 4096], H16 d64, causal + window 1024;
+    two heads checked on every row of every sequence."""
+    c = configs.VARLEN
+    lens = inputs.lengths(c["nseq"], c["len_lo"], c["len_hi"], c["seed"])
+    _varlen_case(lens, c["heads"], c["d"], c["causal"], c["window_left"], c["seed"],
+                 heads_checked=[0, 11])
+
+
+def _decode_case(B, H, max_len, d, lens, chunk, seed, pairs=None):
+    lens = torch.as_tensor(lens, dtype=torch.int32)
+    what = f"decode B{B} H{H} max_len{max_len} d{d} chunk{chunk}"
+    announce(what)
+    kc = inputs.decode_cache(B, max_len, H, d, lens, seed, "cuda", "k")
+    vc = inputs.decode_cache(B, max_len, H, d, lens, seed, "cuda", "v")
+    q = inputs.normal((B, 1, H, d), inputs.subseed(seed, "q")).cuda()
+    s = configs.default_scale(d)
+    o, lse = fa.decode(q, kc, vc, lens.cuda(), scale=s, chunk=chunk)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    o_ref = np.zeros((len(pairs), d))
+    lse_ref = np.zeros(len(pairs))
+    got_o = torch.zeros((len(pairs), d), dtype=torch.bfloat16)
+    got_l = torch.zeros(len(pairs))
+    qn = _np(q.cpu())
+    for i, (b, h) in enumerate(pairs):
+        n = int(lens[b])
+        kn = _np(kc[b, :n, h].cpu())
+        vn = _np(vc[b, :n, h].cpu())
+        ob, lb = oracle.sdpa(qn[b, :, h], kn, vn, s)
+        o_ref[i], lse_ref[i] = ob[0], lb[0]
+        got_o[i], got_l[i] = o[b, 0, h], lse[b, h]
+    check(got_o, got_l, o_ref, lse_ref, torch.bfloat16, what)
+    del kc, vc
+    return q, o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [64, 256, 512])
+def test_decode_small(d, chunk):
+    """Padding rows are NaN: any read past a sequence's length poisons O."""
+    _decode_case(3, 2, 1000, d, [1, 257, 1000], chunk, seed=41)
+
+
+def test_decode_empty_sequence():
+    q, o, lse = _decode_case(2, 2, 64, 128, [0, 5], 64, seed=42, pairs=[(1, 0), (1, 1)])
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_decode_equals_prefill_last_row():
+    """One query against L cached keys is the last row of causal prefill."""
+    L, H, d = 777, 2, 128
+    kc = inputs.decode_cache(1, 1024, H, d, [L], 43, "cuda", "k")
+    vc = inputs.decode_cache(1, 1024, H, d, [L], 43, "cuda", "v")
+    q = inputs.normal((1, 1, H, d), 5).cuda()
+    announce("decode vs prefill")
+    od, ld = fa.decode(q, kc, vc, torch.tensor([L], dtype=torch.int32, device="cuda"), chunk=128)
+    op, lp = fa.attention(q, kc[:, :L].contiguous(), vc[:, :L].contiguous(), causal=True)
+    torch.cuda.synchronize()
+    assert (od.float() - op.float()).abs().max().item() <= 2e-2
+    assert (ld - lp[:, :, 0]).abs().max().item() <= 1e-3
+
+
+def test_workload_decode():
+    """B64 H32, lengths U[1024, 32768], d128, 256-key chunks, full-size NaN
+    padded caches; 8 sequences x 4 heads checked against the oracle."""
+    c = configs.DECODE
+    lens = inputs.lengths(c["batch"], c["len_lo"], c["len_hi"], c["seed"]).to(torch.int32)
+    rng = np.random.default_rng(5)
+    bs = [int(lens.argmax()), int(lens.argmin())] + list(rng.choice(c["batch"], 6, replace=False))
+    pairs = [(int(b), int(h)) for b in bs for h in (0, 7, 19, 31)]
+    _decode_case(c["batch"], c["heads"], c["max_len"], c["d"], lens, c["chunk"], c["seed"], pairs)
+    torch.cuda.empty_cache()
