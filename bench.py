@@ -1,0 +1,451 @@
+#!/usr/bin/env python3
+"""Attention-forward bench on one MI355X.
+
+``python bench.py [--gpus 1] [--steps K] [--warmup W]`` prints ONE JSON line.
+A step is one ``fa_fwd`` launch over the B4 H16 N2048 d128 bf16 non-causal
+prefill workload with its inputs resident in HBM; ``value`` is its
+algorithmic throughput (4 * d FLOPs per allowed (query, key) pair) over K
+timed steps.  The line also carries:
+
+* ``roofline``: the prefill kernel's algorithmic FLOPs per launch divided by
+  its mean launch duration (HIP events on the launch stream) against the
+  dense bf16 matrix-core peak, plus the HBM traffic per launch read from the
+  committed rocprofv3 counter summary when it was taken on the current kernel
+  source (else null);
+* ``cpu_baseline``: the fp64 CPU oracle timed on this host's cores on the
+  same workload;
+* ``secondary``: the other workloads (causal 2k, 8000-token causal prompt,
+  packed varlen with a 1024-key window, fp32 small case, and KV-cache decode
+  in HBM GB/s with its own roofline), each timed the same way.
+
+``--profile-target NAME`` runs only NAME's launches (plus, with
+``--calibrate-copy``, a plain device copy of known size) for rocprofv3.
+``--pmc-summary FETCH_DIR WRITE_DIR`` turns two ``rocprofv3 --pmc`` runs into
+the committed traffic summary under profiles/.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16) and % MFMA peak; decode KV-read HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
+DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
+COPY_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def pairs_dense(n_q, n_k, causal, window):
+    """Allowed (query, key) pairs of one head, closed form per row."""
+    delta = n_k - n_q
+    tot = 0
+    for i in range(n_q):
+        hi = min(n_k - 1, i + delta) if causal else n_k - 1
+        lo = max(0, i + delta - window) if window >= 0 else 0
+        tot += max(0, hi - lo + 1)
+    return tot
+
+
+# ------------------------------------------------------------- workloads
+
+
+class Workload:
+    """Inputs resident on the GPU plus a launch closure and its work figure."""
+
+    def __init__(self, name, launch, work, unit, peak, bound, dtype, config):
+        self.name, self.launch, self.work, self.unit = name, launch, work, unit
+        self.peak, self.bound, self.dtype, self.config = peak, bound, dtype, config
+
+
+def make_dense(torch, fa, inputs, configs, cfg, causal=None, dtype_name="bf16"):
+    B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
+    causal = cfg["causal"] if causal is None else causal
+    W = cfg["window_left"]
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    q, k, v = (x.cuda() for x in inputs.dense_qkv(B, N, N, H, d, cfg["seed"], dt))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    s = configs.default_scale(d)
+    fn = fa.fa_fwd if dtype_name == "bf16" else fa.fa_fwd_fp32
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fn(q, k, v, o, lse, B, H, N, N, d, s, int(causal), W, None, None, stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd")
+
+    flops = 4 * d * H * B * pairs_dense(N, N, causal, W)
+    peak = PEAK_BF16_TFLOPS if dtype_name == "bf16" else PEAK_FP32_TFLOPS
+    name = cfg["name"].replace("_causal", "") + ("_causal" if causal else "")
+    conf = dict(workload=name, batch=B, heads=H, seqlen=N, d=d, causal=bool(causal),
+                window_left=W)
+    return Workload(name, launch, flops, "TFLOP/s", peak, "mfma", dtype_name, conf)
+
+
+def make_varlen(torch, fa, inputs, configs, cfg):
+    lens = inputs.lengths(cfg["nseq"], cfg["len_lo"], cfg["len_hi"], cfg["seed"])
+    cu = inputs.cu_seqlens(lens).cuda()
+    H, d, W = cfg["heads"], cfg["d"], cfg["window_left"]
+    q, k, v = (x.cuda() for x in inputs.varlen_qkv(lens, H, d, cfg["seed"]))
+    o = torch.empty_like(q)
+    total = int(lens.sum())
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    mx = int(lens.max())
+    s = configs.default_scale(d)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fa.fa_fwd(q, k, v, o, lse, len(lens), H, mx, mx, d, s, 1, W, cu, cu, stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd varlen")
+
+    pairs = sum(pairs_dense(int(n), int(n), True, W) for n in lens)
+    conf = dict(workload=cfg["name"], nseq=len(lens), total_tokens=total, heads=H, d=d,
+                causal=True, window_left=W, lengths=[int(x) for x in lens])
+    return Workload(cfg["name"], launch, 4 * d * H * pairs, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma",
+                    "bf16", conf)
+
+
+def make_decode(torch, fa, inputs, configs, cfg):
+    B, H, d, L, chunk = cfg["batch"], cfg["heads"], cfg["d"], cfg["max_len"], cfg["chunk"]
+    lens = inputs.lengths(B, cfg["len_lo"], cfg["len_hi"], cfg["seed"]).to(torch.int32)
+    kc = inputs.decode_cache(B, L, H, d, lens, cfg["seed"], "cuda", "k")
+    vc = inputs.decode_cache(B, L, H, d, lens, cfg["seed"], "cuda", "v")
+    q = inputs.normal((B, 1, H, d), inputs.subseed(cfg["seed"], "q")).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    sl = lens.cuda()
+    need = fa.fa_decode_workspace_size(B, H, L, d, chunk)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = configs.default_scale(d)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fa.fa_decode(q, kc, vc, sl, o, lse, B, H, L, d, s, chunk, ws, need, stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_decode")
+
+    # algorithmic bytes: every valid K and V row once, plus q in and o out
+    kv_bytes = int(lens.sum()) * H * d * 2 * 2
+    byts = kv_bytes + 2 * B * H * d * 2
+    conf = dict(workload=cfg["name"], batch=B, heads=H, d=d, max_len=L, chunk=chunk,
+                kv_rows=int(lens.sum()), kv_bytes=kv_bytes)
+    w = Workload(cfg["name"], launch, byts, "GB/s", PEAK_HBM_GBS, "hbm", "bf16", conf)
+    w.tensors = (kc, vc)
+    return w
+
+
+# ---------------------------------------------------------------- timing
+
+
+def time_launches(torch, w, steps, warmup):
+    """Warm up, then time exactly ``steps`` launches: wall clock between two
+    device synchronisations, and per-launch HIP events on the launch stream."""
+    for _ in range(warmup):
+        w.launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        w.launch()
+        ends[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
+    return (t1 - t0) * 1e3 / steps, statistics.mean(per), min(per)
+
+
+def rate(w, ms):
+    scale = 1e12 if w.unit == "TFLOP/s" else 1e9
+    return w.work / (ms * 1e-3) / scale
+
+
+def read_traffic(summary, src):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is absent or was taken on another version of the kernel source."""
+    if not os.path.exists(summary):
+        return None
+    vals = {}
+    with open(summary) as f:
+        for line in f:
+            if ":" in line:
+                key, _, val = line.partition(":")
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_source_sha256") != sha256(src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg):
+    """The fp64 oracle, as it stands, on every (batch, head) slice of the
+    headline workload, timed on this host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from io_aware_exact_19_amd import configs, inputs
+
+    B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
+    q, k, v = inputs.dense_qkv(B, N, N, H, d, cfg["seed"])
+    qn, kn, vn = (x.float().double().numpy() for x in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.attention_dense(qn, kn, vn, configs.default_scale(d), False, -1)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    flops = 4 * d * H * B * N * N
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"all {B * H} (batch, head) slices of the B{B} H{H} N{N} d{d} non-causal "
+                       f"workload once: {dt:.2f} s, fp64, score matrix materialised",
+                seconds=round(dt, 3), host_cpus=len(os.sched_getaffinity(0)))
+
+
+# ----------------------------------------------------- counter summaries
+
+
+def _pmc_rows(d):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_kernel(rows, counter):
+    """Counter values per kernel name, in dispatch order."""
+    out = {}
+    rows = sorted(rows, key=lambda r: int(r.get("Dispatch_Id", 0)))
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r.get("Kernel_Name", "")
+        out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, target, out_path, cmd):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the target kernel,
+    each scaled by what the counter reads for a device copy of COPY_BYTES."""
+    fetch = _per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
+
+    def pick(d, key):
+        names = [n for n in d if key in n]
+        if not names:
+            raise SystemExit(f"no kernel matching {key!r} in {sorted(d)}")
+        return names[0], d[names[0]]
+
+    kname = "fwd_bf16_kernel" if target.startswith("prefill") else "decode_split_kernel"
+    fk, fvals = pick(fetch, kname)
+    _, wvals = pick(write, kname)
+    # the calibration copies are the last three device-to-device copies of the run
+    ck, cf = pick(fetch, "copyBuffer")
+    _, cw = pick(write, ck)
+    cf, cw = cf[-3:], cw[-3:]
+    f_kib, w_kib = statistics.median(fvals), statistics.median(wvals)
+    cf_kib, cw_kib = statistics.median(cf), statistics.median(cw)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    extra = []
+    if target.startswith("decode"):
+        cb = [n for n in fetch if "decode_combine_kernel" in n]
+        if cb:
+            extra.append(("combine_fetch_kib_per_dispatch", statistics.median(fetch[cb[0]])))
+    hbm = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
+    src = PREFILL_KERNEL_SRC if target.startswith("prefill") else DECODE_KERNEL_SRC
+    lines = [
+        f"# HBM traffic of {fk.replace('void fa::(anonymous namespace)::', '').split('(fa::')[0]}"
+        f" ({target} workload) from two rocprofv3 --pmc passes",
+        f"command: {cmd}",
+        f"kernel: {fk}",
+        f"dispatches_fetch: {len(fvals)}",
+        f"dispatches_write: {len(wvals)}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"copy_kernel: {ck}",
+        f"copy_bytes_read_and_written: {COPY_BYTES}",
+        f"copy_fetch_kib: {cf_kib:.1f}",
+        f"copy_write_kib: {cw_kib:.1f}",
+        f"fetch_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        *[f"{k}: {v:.1f}" for k, v in extra],
+        f"hbm_bytes_per_launch: {hbm:.0f}",
+        f"kernel_source_sha256: {sha256(src)}",
+    ]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile-target", default=None,
+                    choices=["prefill_2k", "prefill_2k_causal", "long_8k", "varlen", "small_fp32",
+                             "decode"])
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-target", default="prefill_2k")
+    ap.add_argument("--pmc-out", default=None)
+    ap.add_argument("--pmc-cmd", default="")
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        out = args.pmc_out or (TRAFFIC_SUMMARY if args.pmc_target.startswith("prefill")
+                               else DECODE_TRAFFIC_SUMMARY)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_target, out, args.pmc_cmd)
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("this bench measures one GPU only: the attention forward path is built and "
+              "measured on a single MI355X (heads and batch entries shard across GPUs with no "
+              "exchange); run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import io_aware_exact_19_amd as fa
+    from io_aware_exact_19_amd import configs, inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    fa.load_library()
+    dev = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {dev.name} CUs {dev.multi_processor_count}")
+
+    builders = {
+        "prefill_2k": lambda: make_dense(torch, fa, inputs, configs, configs.PREFILL_2K, False),
+        "prefill_2k_causal": lambda: make_dense(torch, fa, inputs, configs, configs.PREFILL_2K,
+                                                True),
+        "long_8k": lambda: make_dense(torch, fa, inputs, configs, configs.LONG_8K),
+        "varlen": lambda: make_varlen(torch, fa, inputs, configs, configs.VARLEN),
+        "small_fp32": lambda: make_dense(torch, fa, inputs, configs, configs.SMALL_FP32,
+                                         dtype_name="f32"),
+        "decode": lambda: make_decode(torch, fa, inputs, configs, configs.DECODE),
+    }
+
+    if args.profile_target:
+        w = builders[args.profile_target]()
+        wall, mean_ms, min_ms = time_launches(torch, w, args.steps, args.warmup)
+        log(f"[profile] {w.name}: {args.steps} launches, mean {mean_ms:.4f} ms, "
+            f"{rate(w, mean_ms):.2f} {w.unit}")
+        if args.calibrate_copy:
+            src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[profile] copied {COPY_BYTES} bytes x3")
+        return 0
+
+    # ---- headline: B4 H16 N2048 d128 bf16 non-causal prefill
+    head = builders["prefill_2k"]()
+    log(f"[bench] timing {head.name}: warmup {args.warmup}, steps {args.steps}")
+    wall_ms, mean_ms, min_ms = time_launches(torch, head, args.steps, args.warmup)
+    achieved = rate(head, mean_ms)
+    traffic = read_traffic(TRAFFIC_SUMMARY, PREFILL_KERNEL_SRC)
+    result = {
+        "metric": METRIC,
+        "value": round(head.work / (wall_ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) bf16 Q/K/V from fixed seeds, inputs resident in HBM",
+        "config": head.config,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "fwd_bf16_kernel<128,false>",
+            "flops_per_launch": head.work,
+            "mean_launch_ms": round(mean_ms, 5),
+            "min_launch_ms": round(min_ms, 5),
+        },
+    }
+    log(f"[bench] {head.name}: {result['value']} TFLOP/s wall, kernel {achieved:.1f} TFLOP/s")
+    del head
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = []
+        for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode"):
+            w = builders[key]()
+            steps = 20 if key != "decode" else 10
+            log(f"[bench] timing {w.name}")
+            wall, mean2, min2 = time_launches(torch, w, steps, 3)
+            r = rate(w, mean2)
+            entry = {"workload": w.name, "value": round(r, 3), "unit": w.unit,
+                     "frac_of_peak": round(r / w.peak, 4), "peak": w.peak, "bound": w.bound,
+                     "dtype": w.dtype, "mean_launch_ms": round(mean2, 5),
+                     "min_launch_ms": round(min2, 5), "steps": steps}
+            if key == "decode":
+                entry["kv_bytes_per_launch"] = w.config["kv_bytes"]
+                entry["traffic"] = read_traffic(DECODE_TRAFFIC_SUMMARY, DECODE_KERNEL_SRC)
+            if key == "varlen":
+                entry["lengths"] = w.config["lengths"]
+            sec.append(entry)
+            log(f"[bench] {w.name}: {r:.2f} {w.unit} ({100 * r / w.peak:.1f}% of peak)")
+            del w
+            torch.cuda.empty_cache()
+        result["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the headline workload")
+        result["cpu_baseline"] = cpu_baseline(configs.PREFILL_2K)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
