@@ -23,8 +23,13 @@
 //    probabilities are already the k-slots the P V product wants: no data
 //    movement between the two products.
 //  * The softmax works in base 2 with log2(e) folded into the scale
-//    (v_exp_f32), and divides once per row at the end.
-//  * K and V tiles are double buffered in LDS; V is stored transposed.
+//    (v_exp_f32), moves its reference max only when a row max grows by more
+//    than 2^8, and divides once per row at the end.
+//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//    destination, no register staging; rows past the sequence end come back
+//    as zeros from the descriptor bound), double buffered, one barrier per
+//    tile.  V stays row-major in LDS: the P V operand is read with the
+//    transposing LDS read (ds_read_b64_tr_b16).
 //  * Fully masked K/V tiles (causal, sliding window) are never loaded;
 //    element masks run only on tiles that cross a mask boundary.
 #include "fa_common.h"
@@ -43,11 +48,6 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int pi_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
-
-// 16-byte-chunk XOR swizzles of the LDS tiles (bank spreading for the MFMA
-// operand reads and the tile stores).
-__device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8); }
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 // Per-workgroup work item.
 struct Work {
@@ -119,35 +119,83 @@ __device__ bool varlen_work(const FwdArgs& a, int lane, Work& w) {
   return false;
 }
 
+// One K or V tile in LDS: kBC rows x D bf16, row-major as in HBM; 16-byte
+// chunk c of row r sits at chunk position c ^ tile_swz(r) so that the MFMA
+// operand reads of a wave spread over the LDS banks.
 template <int D>
 struct BfTile {
-  static constexpr int kKch = D / 8;                      // 16-byte chunks per K row
-  static constexpr int kKBytes = kBC * D * 2;             // one K tile
-  static constexpr int kVBytes = kBC * D * 2;             // one V^T tile
-  static constexpr int kKLoads = kBC * kKch / kThreads;   // 16-byte K loads per thread
-  static constexpr int kVBlocks = (kBC / 4) * (D / 8);    // 4-key x 8-dim V blocks
-  static constexpr int kVIters = (kVBlocks + kThreads - 1) / kThreads;
-  static constexpr int kLds = 2 * (kKBytes + kVBytes);    // double buffered
-  static_assert(kBC * kKch % kThreads == 0, "K tile must split evenly");
+  static constexpr int kKch = D / 8;                    // 16-byte chunks per row
+  static constexpr int kBytes = kBC * D * 2;            // one tile
+  static constexpr int kLoads = kBytes / 16 / kThreads; // 16-byte DMA loads per thread per tile
+  static_assert(kBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
 };
 
-// V block id -> (c8: 8-dim chunk, g: 4-key group).  Within 16 consecutive
-// threads c8 takes 8 values and g two, so the transposed 8-byte LDS stores
-// of those threads land in 16 distinct bank slots.
-template <int D>
-__device__ __forceinline__ void vblock_coords(int blk, int& c8, int& g) {
-  constexpr int kHi = D / 64;  // 8-dim chunks beyond the first 8
-  const int rest = blk >> 4;
-  c8 = (blk & 7) + 8 * (rest % kHi);
-  g = ((blk >> 3) & 1) + 2 * (rest / kHi);
+__device__ __forceinline__ int tile_swz(int r) {
+  return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8);
 }
+
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * (D * 2) + ((c ^ tile_swz(r)) & (D / 8 - 1)) * 16;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Queue the DMA of K/V tile rows [k0, k0 + kBC) of one head straight into
+// LDS (no registers).  The buffer descriptor covers only the rows that exist,
+// so rows past the sequence end read as zeros without a branch.
+template <int D>
+__device__ __forceinline__ void issue_tile(const uint16_t* kg, const uint16_t* vg, long long rs,
+                                           int k0, int n_k, char* kdst, char* vdst, int wave,
+                                           int lane) {
+  using T = BfTile<D>;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t nrec = (uint32_t)min(n_k - k0, kBC) * row_bytes;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) {
+    const int blk = i * 4 + wave;  // 1 KB block of the tile written by this wave
+    const int slot = blk * 64 + lane;
+    const int r = slot / T::kKch;
+    const int c = ((slot % T::kKch) ^ tile_swz(r)) & (T::kKch - 1);
+    const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// Lane-half exchange on the VALU: {r0, r1} = {x[lane], x[lane ^ 32]}.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running max is moved only when a row's new max exceeds it by more than
+// this (base-2 units): the output u / l does not depend on which reference
+// max is used, and probabilities stay <= 2^8, far from fp32/bf16 overflow.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   using T = BfTile<D>;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[T::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
+  const int grp = lane >> 4, j16 = lane & 15;
 
   Work w;
   if constexpr (VARLEN) {
@@ -184,19 +232,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (W >= 0) w_lo = max(w_lo, wq0 + delta - W);
   const int qi = wq0 + l32;  // this lane's query row
 
-  // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]
+  // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
+  // the sequence read as zeros through the descriptor bound
   bf16x8_t qf[D / 16];
   {
-    const bool ok = qi < n_q;
-    const uint16_t* p = qg + (long long)qi * rs + half * 8;
+    const uint32_t row_bytes = (uint32_t)(rs * 2);
+    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      if (ok) {
-        qf[kk] = *(const bf16x8_t*)(p + kk * 16);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qf[kk][t] = (__bf16)0.0f;
-      }
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
@@ -205,167 +253,132 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  float m_run = kNegInf;  // running max of this row (base-2 scaled)
+  float m_run = kNegInf;  // reference max of this row (base-2 scaled)
   float l_run = 0.0f;     // partial exp-sum over this lane-half's keys
 
-  char* const lds_k0 = lds;
-  char* const lds_v0 = lds + 2 * T::kKBytes;
+  // per-lane parts of the LDS operand addresses
+  int k_off[D / 16][kBC / 32];  // K rows enter in pi order (see pi_row)
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb) k_off[kk][kb] = tile_off<D>(kb * 32 + pi_row(l32), kk * 2 + half);
+  // V^T fragments through the transposing read: lane j of 16-lane group g
+  // addresses row (ks*16 + 8*(g/2) + 4*u + j/4), dims db*32 + 16*(g%2) + 4*(j%4)
+  int v_off[D / 32][kBC / 16][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int ks = 0; ks < kBC / 16; ++ks)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = ks * 16 + 8 * (grp >> 1) + 4 * u + (j16 >> 2);
+        const int d = db * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
+        v_off[db][ks][u] = tile_off<D>(r, d >> 3) + (d & 7) * 2;
+      }
 
-  u32x4_t kreg[T::kKLoads];
-  u32x4_t vreg[T::kVIters][4];
-
-  auto load_tile = [&](int kt) {
+  // one K/V tile: S^T = K Q^T, mask, online softmax update, O^T += V^T P^T
+  auto compute_tile = [&](int kt, const char* kb_lds, const char* vb_lds) {
     const int k0 = kt * kBC;
+    if (!(wave_live && k0 < w_hi && k0 + kBC > w_lo)) return;
+    f32x16_t sacc[kBC / 32];
 #pragma unroll
-    for (int i = 0; i < T::kKLoads; ++i) {
-      const int id = i * kThreads + tid;
-      const int r = id / T::kKch, c = id % T::kKch;
-      const int key = k0 + r;
-      kreg[i] = key < n_k ? *(const u32x4_t*)(kg + (long long)key * rs + c * 8)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
-    for (int i = 0; i < T::kVIters; ++i) {
-      const int blk = i * kThreads + tid;
-      int c8, g;
-      vblock_coords<D>(blk, c8, g);
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * g + j;
-        vreg[i][j] = (blk < T::kVBlocks && key < n_k)
-                         ? *(const u32x4_t*)(vg + (long long)key * rs + c8 * 8)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < kBC / 32; ++kb) {
+        const bf16x8_t kf = *(const bf16x8_t*)(kb_lds + k_off[kk][kb]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
       }
     }
-  };
 
-  auto store_tile = [&](int buf) {
-    char* kd = lds_k0 + buf * T::kKBytes;
+    // element mask, only on tiles crossing a mask boundary
+    const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
+                           (W >= 0 && k0 < wq_last + delta - W);
+    if (need_mask) {
 #pragma unroll
-    for (int i = 0; i < T::kKLoads; ++i) {
-      const int id = i * kThreads + tid;
-      const int r = id / T::kKch, c = id % T::kKch;
-      *(u32x4_t*)(kd + r * (D * 2) + ((c ^ k_swz(r)) & (T::kKch - 1)) * 16) = kreg[i];
-    }
-    char* vd = lds_v0 + buf * T::kVBytes;
+      for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
-    for (int i = 0; i < T::kVIters; ++i) {
-      const int blk = i * kThreads + tid;
-      if (blk < T::kVBlocks) {
-        int c8, g;
-        vblock_coords<D>(blk, c8, g);
-#pragma unroll
-        for (int dp = 0; dp < 8; ++dp) {
-          const int word = dp >> 1;
-          const uint32_t sel = (dp & 1) ? 0x07060302u : 0x05040100u;
-          u32x2_t pr;
-          pr[0] = __builtin_amdgcn_perm(vreg[i][1][word], vreg[i][0][word], sel);
-          pr[1] = __builtin_amdgcn_perm(vreg[i][3][word], vreg[i][2][word], sel);
-          const int d = c8 * 8 + dp;
-          *(u32x2_t*)(vd + d * (kBC * 2) + (((g >> 1) ^ v_swz(d)) & 7) * 16 + (g & 1) * 8) = pr;
+        for (int r = 0; r < 16; ++r) {
+          const int kj = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
+          const bool ok = kj < n_k && (!causal || kj <= qi + delta) &&
+                          (W < 0 || kj >= qi + delta - W);
+          if (!ok) sacc[kb][r] = kNegInf;
         }
+    }
+
+    // online softmax update, base 2, lazy reference max
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    const float m_tile = max_halves(mx) * c2;
+    const bool grow = m_tile > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = grow ? exp2_hw(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.0f : m_run;
+    float rsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(fmaf(sacc[kb][r], c2, -m_use));
+        sacc[kb][r] = p;
+        rsum += p;
+      }
+    l_run += rsum;
+
+#pragma unroll
+    for (int ks = 0; ks < kBC / 16; ++ks) {
+      const int kb = ks >> 1, o8 = (ks & 1) * 8;
+      const bf16x8_t pf =
+          to_bf16x8(sacc[kb][o8 + 0], sacc[kb][o8 + 1], sacc[kb][o8 + 2], sacc[kb][o8 + 3],
+                    sacc[kb][o8 + 4], sacc[kb][o8 + 5], sacc[kb][o8 + 6], sacc[kb][o8 + 7]);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vb_lds + v_off[db][ks][0]));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(vb_lds + v_off[db][ks][1]));
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
       }
     }
   };
 
   if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int kt = t_lo; kt < t_hi; ++kt) {
-    const int buf = (kt - t_lo) & 1;
-    const bool more = kt + 1 < t_hi;
-    if (more) load_tile(kt + 1);
-    const int k0 = kt * kBC;
-
-    if (wave_live && k0 < w_hi && k0 + kBC > w_lo) {
-      // ---- S^T = K Q^T for this tile (raw scores, fp32)
-      const char* kb_lds = lds_k0 + buf * T::kKBytes;
-      f32x16_t sacc[kBC / 32];
-#pragma unroll
-      for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < kBC / 32; ++kb) {
-          const int r = kb * 32 + pi_row(l32);
-          const int c = kk * 2 + half;
-          const bf16x8_t kf =
-              *(const bf16x8_t*)(kb_lds + r * (D * 2) + ((c ^ k_swz(r)) & (T::kKch - 1)) * 16);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sacc[kb], 0, 0, 0);
-        }
-      }
-
-      // ---- element mask, only on tiles crossing a mask boundary
-      const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
-                             (W >= 0 && k0 < wq_last + delta - W);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kj = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-            const bool ok = kj < n_k && (!causal || kj <= qi + delta) &&
-                            (W < 0 || kj >= qi + delta - W);
-            if (!ok) sacc[kb][r] = kNegInf;
-          }
-      }
-
-      // ---- online softmax update (base 2)
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * c2);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = exp2_hw(m_run - m_use);
-      float rsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < kBC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_hw(fmaf(sacc[kb][r], c2, -m_use));
-          sacc[kb][r] = p;
-          rsum += p;
-        }
-      l_run = fmaf(l_run, alpha, rsum);
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // ---- O^T += V^T P^T
-      const char* vb_lds = lds_v0 + buf * T::kVBytes;
-#pragma unroll
-      for (int ks = 0; ks < kBC / 16; ++ks) {
-        const int kb = ks >> 1, o8 = (ks & 1) * 8;
-        const bf16x8_t pf =
-            to_bf16x8(sacc[kb][o8 + 0], sacc[kb][o8 + 1], sacc[kb][o8 + 2], sacc[kb][o8 + 3],
-                      sacc[kb][o8 + 4], sacc[kb][o8 + 5], sacc[kb][o8 + 6], sacc[kb][o8 + 7]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int dd = db * 32 + l32;
-          const int kc = ks * 2 + half;
-          const bf16x8_t vf =
-              *(const bf16x8_t*)(vb_lds + dd * (kBC * 2) + ((kc ^ v_swz(dd)) & 7) * 16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[db], 0, 0, 0);
-        }
+    issue_tile<D>(kg, vg, rs, t_lo * kBC, n_k, k_lds0, v_lds0, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile t_lo are in
+    __syncthreads();
+    // two tiles per trip so that each buffer is a distinct LDS object
+    for (int kt = t_lo; kt < t_hi; kt += 2) {
+      if (kt + 1 < t_hi) issue_tile<D>(kg, vg, rs, (kt + 1) * kBC, n_k, k_lds1, v_lds1, wave, lane);
+      compute_tile(kt, k_lds0, v_lds0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (kt + 1 < t_hi) {
+        if (kt + 2 < t_hi) issue_tile<D>(kg, vg, rs, (kt + 2) * kBC, n_k, k_lds0, v_lds0, wave, lane);
+        compute_tile(kt + 1, k_lds1, v_lds1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
       }
     }
-
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: O = u / l (one division per row), lse = ln 2 * (m + log2 l)
-  const float l_tot = l_run + swap_halves(l_run);
+  // epilogue: O = u / l (one division per row), lse = ln 2 * (m + log2 l)
+  const float l_tot = sum_halves(l_run);
   if (qi < n_q) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     uint16_t* op = og + (long long)qi * rs;
@@ -531,20 +544,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
 
 template <int D, bool VARLEN>
 hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
-  using T = BfTile<D>;
   const int nqt = ceil_div(a.seqlen_q, kBR);
   const long long grid = (long long)a.batch * a.heads * nqt;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  auto kern = fwd_bf16_kernel<D, VARLEN>;
-  static bool attr_set = false;  // benign race: idempotent attribute
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), T::kLds, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
