@@ -29,7 +29,9 @@
 //    destination, no register staging; rows past the sequence end come back
 //    as zeros from the descriptor bound), double buffered, one barrier per
 //    tile.  V stays row-major in LDS: the P V operand is read with the
-//    transposing LDS read (ds_read_b64_tr_b16).
+//    transposing LDS read (ds_read_b64_tr_b16).  K and V use different
+//    16-byte-chunk swizzles, each chosen so that its own read pattern is free
+//    of LDS bank conflicts.
 //  * Fully masked K/V tiles (causal, sliding window) are never loaded;
 //    element masks run only on tiles that cross a mask boundary.
 #include "fa_common.h"
@@ -139,6 +141,18 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * (D * 2) + ((c ^ tile_swz(r)) & (D / 8 - 1)) * 16;
 }
 
+// V tiles are read only through the transposing read, whose 16-lane groups
+// touch 4 consecutive rows x 2 adjacent chunks: spread those rows over
+// distinct bank groups (bits 1-3 of the chunk index).
+__device__ __forceinline__ int vtile_swz(int r) {
+  return (0xAC60 >> ((r & 3) * 4)) & 15;  // {0, 6, 12, 10}
+}
+
+template <int D>
+__device__ __forceinline__ int vtile_off(int r, int c) {
+  return r * (D * 2) + ((c ^ vtile_swz(r)) & (D / 8 - 1)) * 16;
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -165,8 +179,10 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kg, const uint16_t* v
     const int slot = blk * 64 + lane;
     const int r = slot / T::kKch;
     const int c = ((slot % T::kKch) ^ tile_swz(r)) & (T::kKch - 1);
-    const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)c * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, voff, 0, 0, 0);
+    const int cv = ((slot % T::kKch) ^ vtile_swz(r)) & (T::kKch - 1);
+    const uint32_t koff = (uint32_t)r * row_bytes + (uint32_t)c * 16;
+    const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16, koff, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16, voff, 0, 0, 0);
   }
 }
@@ -273,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int r = ks * 16 + 8 * (grp >> 1) + 4 * u + (j16 >> 2);
         const int d = db * 32 + 16 * (grp & 1) + 4 * (j16 & 3);
-        v_off[db][ks][u] = tile_off<D>(r, d >> 3) + (d & 7) * 2;
+        v_off[db][ks][u] = vtile_off<D>(r, d >> 3) + (d & 7) * 2;
       }
 
   // one K/V tile: S^T = K Q^T, mask, online softmax update, O^T += V^T P^T
