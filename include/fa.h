@@ -52,7 +52,8 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, scale not finite > 0 */
-  FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: head dim, chunk size, varlen+fp32 */
+  FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: head dim, chunk size, varlen+fp32,
+                              a grid over 2^31 workgroups, a key row (heads*d) over 64 MiB */
   FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required */
   FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
 } fa_status;

@@ -34,7 +34,14 @@ int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, 
   const long long grid = (long long)batch * heads * ((seqlen_q + 127) / 128);
   if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
 
+  // K/V rows are addressed with 32-bit byte offsets inside windows of
+  // seg_rows rows; one 64-row tile must fit a window
+  const unsigned long long row_bytes = (unsigned long long)heads * d * (fp32 ? 4 : 2);
+  const unsigned long long win = 0xFFFFFFFFull / row_bytes;
+  if (win < 64) return FA_ERR_UNSUPPORTED;
+
   fa::FwdArgs a;
+  a.seg_rows = (int)((win > (1ull << 30) ? (1ull << 30) : win) & ~63ull);
   a.q = q;
   a.k = k;
   a.v = v;

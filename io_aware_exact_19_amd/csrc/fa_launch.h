@@ -21,6 +21,7 @@ struct FwdArgs {
   int window_left;
   const int* cu_q;  // varlen offsets, NULL for dense
   const int* cu_k;
+  int seg_rows;     // key rows one 32-bit-offset buffer window covers (multiple of 64)
 };
 
 struct DecodeArgs {

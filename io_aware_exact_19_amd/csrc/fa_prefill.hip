@@ -12,37 +12,67 @@
 // then for each K/V block compute local scores, update row max and
 // normaliser, accumulate the output; write the output once at the end.
 //
-// gfx950 mapping (not from the pages):
-//  * 4 waves x 32 query rows per workgroup; each wave owns whole rows, so row
-//    statistics need no LDS traffic (one lane-half swap per tile for the max).
-//  * Scores are produced transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
-//    each lane then holds 16 keys of a single query row, so the row max/sum is
-//    mostly in-lane, and the output accumulator O^T = V^T P^T gives each lane
-//    a single query row as well (one rescale factor per lane).
+// gfx950 mapping (not from the pages).  Common to both bf16 kernels:
+//  * Each wave owns 32 whole query rows, so row statistics need no LDS
+//    traffic.  Scores are produced transposed, S^T = K Q^T, on
+//    v_mfma_f32_32x32x16_bf16: each lane then holds the keys of a single
+//    query row, so the row max/sum is in-lane plus one lane-half swap, and
+//    the output accumulator O^T = V^T P^T gives each lane a single query row
+//    as well.
 //  * K rows enter the score product in a permuted order so that a lane's
 //    probabilities are already the k-slots the P V product wants: no data
 //    movement between the two products.
 //  * The softmax works in base 2 with log2(e) folded into the scale
-//    (v_exp_f32), moves its reference max only when a row max grows by more
-//    than 2^8, and divides once per row at the end.
-//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
-//    destination, no register staging; rows past the sequence end come back
-//    as zeros from the descriptor bound), double buffered, one barrier per
-//    tile.  V stays row-major in LDS: the P V operand is read with the
-//    transposing LDS read (ds_read_b64_tr_b16).  K and V use different
-//    16-byte-chunk swizzles, each chosen so that its own read pattern is free
-//    of LDS bank conflicts.
+//    (v_exp_f32); the reference max is lazy (below) and the division by the
+//    row sum happens once per row at the end.
+//  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads
+//    with the LDS destination, no register staging; rows past the sequence
+//    end come back as zeros from the descriptor bound).  V stays row-major in
+//    LDS and the P V operand is read with the transposing LDS read
+//    (ds_read_b64_tr_b16).  K and V use different 16-byte-chunk swizzles,
+//    each free of bank conflicts for its own read pattern.
 //  * Fully masked K/V tiles (causal, sliding window) are never loaded;
 //    element masks run only on tiles that cross a mask boundary.
+//
+// d = 128: ping-pong kernel.  8 waves (256 query rows) per workgroup, two per
+//    SIMD.  The waves form two groups, one wave of each on every SIMD; work
+//    alternates between a matrix block (P V of the previous tile and S of the
+//    current one: 32 MFMAs per wave, operands streamed from LDS a few
+//    products ahead) and a vector block (mask, online-softmax update, bf16
+//    probabilities).  Group 1 runs half a step behind group 0 and a
+//    workgroup barrier between the blocks keeps that offset, so on every
+//    SIMD one wave's matrix block runs next to the other wave's softmax; the
+//    wave in its matrix block raises its issue priority.  Tiles stream
+//    through a ring of four LDS slots two tiles ahead of use; the loads are
+//    queued with inline assembly so that the only waits for them are the
+//    explicit ones before each step's barrier.
+// d = 64: four-wave kernel.  4 waves (128 query rows) per workgroup, two
+//    workgroups per CU, double-buffered tiles, one barrier per tile.  At
+//    d = 64 the softmax work per tile is as large as at d = 128 while the
+//    matrix work halves, so the ping-pong split does not pay there.
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBR = 128;      // query rows per workgroup
-constexpr int kBC = 64;       // keys per K/V tile
-constexpr int kThreads = 256;
+constexpr int kBC = 64;  // keys per K/V tile
+
+// bf16 ping-pong kernel (d = 128)
+constexpr int kWaves = 8;                // two groups of 4, one wave of each per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kBR = kWaves * 32;         // query rows per workgroup
+
+// bf16 four-wave kernel (d = 64)
+constexpr int kQWaves = 4;
+constexpr int kQThreads = kQWaves * 64;
+constexpr int kQRows = kQWaves * 32;
+
+// fp32 kernel geometry
+constexpr int kWaves32 = 4;
+constexpr int kThreads32 = kWaves32 * 64;
+constexpr int kBR32 = kWaves32 * 32;
+constexpr int kBC32 = 32;
 
 // Row order of a 32-key block in the score product: bits 2 and 3 of the row
 // index swapped.  Accumulator register r of lane-half h then holds key
@@ -76,16 +106,16 @@ __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
 }
 
 // Variable-length scheduler: every wave scans the per-sequence tile counts
-// ceil(len_q / kBR) from cu_seqlens_q (no host round trip), drops the
+// ceil(len_q / rows) from cu_seqlens_q (no host round trip), drops the
 // workgroups past the live total, renumbers the rest XCD-contiguously and
 // finds its (head, sequence, tile).  Head-major order keeps the tiles of one
 // (sequence, head) on one XCD.
-__device__ bool varlen_work(const FwdArgs& a, int lane, Work& w) {
+__device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
   const int nseq = a.batch;
   int total = 0;
   for (int s0 = 0; s0 < nseq; s0 += 64) {
     const int s = s0 + lane;
-    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), kBR) : 0;
+    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), rows) : 0;
     const int inc = wave_inclusive_scan(nt, lane);
     total += __shfl(inc, 63, 64);
   }
@@ -97,7 +127,7 @@ __device__ bool varlen_work(const FwdArgs& a, int lane, Work& w) {
   int base = 0;
   for (int s0 = 0; s0 < nseq; s0 += 64) {
     const int s = s0 + lane;
-    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), kBR) : 0;
+    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), rows) : 0;
     const int inc = wave_inclusive_scan(nt, lane) + base;
     const int exc = inc - nt;
     const unsigned long long hit = __ballot(s < nseq && g >= exc && g < inc);
@@ -121,17 +151,18 @@ __device__ bool varlen_work(const FwdArgs& a, int lane, Work& w) {
   return false;
 }
 
-// One K or V tile in LDS: kBC rows x D bf16, row-major as in HBM; 16-byte
-// chunk c of row r sits at chunk position c ^ tile_swz(r) so that the MFMA
-// operand reads of a wave spread over the LDS banks.
-template <int D>
+// One K or V tile in LDS: kBC rows x D bf16, row-major as in HBM, with the
+// 16-byte chunks of each row permuted (swizzled) per row.
+template <int D, int THREADS>
 struct BfTile {
-  static constexpr int kKch = D / 8;                    // 16-byte chunks per row
-  static constexpr int kBytes = kBC * D * 2;            // one tile
-  static constexpr int kLoads = kBytes / 16 / kThreads; // 16-byte DMA loads per thread per tile
-  static_assert(kBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
+  static constexpr int kKch = D / 8;                     // 16-byte chunks per row
+  static constexpr int kBytes = kBC * D * 2;             // one tile
+  static constexpr int kLoads = kBytes / 16 / THREADS;   // 16-byte DMA loads per thread per tile
+  static_assert(kBytes % (16 * THREADS) == 0, "tile must split evenly over the threads");
 };
 
+// K tiles: chunk c of row r at c ^ tile_swz(r).  The score product's
+// 16-lane groups read one chunk of 16 rows whose swizzles are all distinct.
 __device__ __forceinline__ int tile_swz(int r) {
   return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8);
 }
@@ -159,14 +190,485 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+// Raw buffer descriptor over [base, base + bytes).
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// 16 bytes per lane from the buffer (byte offset voff) straight into LDS at
+// lds_base + 16 * lane; offsets past the descriptor's size read as zeros.
+// Issued as inline assembly so that the compiler does not track it: every
+// wait for these loads is an explicit vmcnt wait before a barrier, and LDS
+// reads of other ring slots never wait for them.  M0 (the LDS destination)
+// is saved and restored around the load.
+__device__ __forceinline__ void dma16(const u32x4_t& rsrc_in, uint32_t voff, uint32_t lds_base) {
+  u32x4_t rsrc;  // uniform by construction; keep it in scalar registers
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)p);
+}
+
+// Lane-half exchange on the VALU: {r0, r1} = {x[lane], x[lane ^ 32]}.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lazy reference maximum: the output u / l does not depend on which reference
+// value the exponentials are taken against, so a tile is exponentiated
+// against the current reference and kept when each lane's probabilities sum
+// to at most this bound; probabilities then stay <= 2^16, far from fp32 /
+// bf16 overflow.
+constexpr float kLazyBound = 65536.0f;
+
+// Reductions over N x 16 values with independent partial results (short
+// dependency chains: the vector block runs while its SIMD's other wave
+// keeps the matrix pipe busy, so its latency is not hidden by another wave).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&v)[N][16]) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = v[0][2 * i] + v[0][2 * i + 1];
+#pragma unroll
+  for (int n = 1; n < N; ++n)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] += v[n][2 * i] + v[n][2 * i + 1];
+  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+template <int N>
+__device__ __forceinline__ float tree_max(const f32x16_t (&v)[N]) {
+  float a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = fmaxf(fmaxf(v[0][4 * i], v[0][4 * i + 1]), fmaxf(v[0][4 * i + 2], v[0][4 * i + 3]));
+#pragma unroll
+  for (int n = 1; n < N; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = fmaxf(a[i], fmaxf(fmaxf(v[n][4 * i], v[n][4 * i + 1]), fmaxf(v[n][4 * i + 2], v[n][4 * i + 3])));
+  return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+}
+
+// Sum of the bf16-rounded values of N x 16 floats: pairs rounded to bf16
+// (the same rounding as the P V operand) and summed by dot products with
+// (1, 1) accumulated in fp32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ float sum_rounded(const float (&v)[N][16]) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x2_t pr = {(__bf16)v[n][2 * i], (__bf16)v[n][2 * i + 1]};
+      a[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, a[i & 3], false);
+    }
+  return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// s_waitcnt immediates: wait until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier that is also a compiler memory barrier but carries no
+// implicit wait: the tile loads that must have landed are waited for
+// explicitly (vmcnt) before it, so loads of later tiles stay in flight.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int D, bool VARLEN>
+__device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
+  using T = BfTile<D, kThreads>;
+  // ring of 4 tile slots; slot s holds K at s * 2 * kBytes and V right after
+  __shared__ __attribute__((aligned(1024))) char ring[4 * 2 * T::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int group = wave >> 2;                 // 0: matrix block first; 1: half a tile later
+  const int rblk = 2 * (wave & 3) + group;     // the two waves of a SIMD own adjacent rows
+  const int half = lane >> 5, l32 = lane & 31;
+  const int lg = lane >> 4, j16 = lane & 15;
+
+  Work w;
+  if constexpr (VARLEN) {
+    if (!varlen_work(a, kBR, lane, w)) return;
+  } else {
+    dense_work(a, ceil_div(a.seqlen_q, kBR), w);
+  }
+
+  const long long rs = (long long)a.heads * D;  // elements between consecutive rows
+  const uint16_t* qg = (const uint16_t*)a.q + (w.q_row0 * a.heads + w.h) * D;
+  const uint16_t* kg = (const uint16_t*)a.k + (w.k_row0 * a.heads + w.h) * D;
+  const uint16_t* vg = (const uint16_t*)a.v + (w.k_row0 * a.heads + w.h) * D;
+  uint16_t* og = (uint16_t*)a.o + (w.q_row0 * a.heads + w.h) * D;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+
+  const int n_q = w.n_q, n_k = w.n_k, delta = n_k - n_q;
+  const int causal = a.causal, W = a.window_left;
+  const float c2 = a.scale_log2;
+  const int q0 = w.qt * kBR;
+  const int q_last = min(q0 + kBR, n_q) - 1;
+
+  // K/V tiles the workgroup needs (fully masked ones are skipped)
+  int kv_lo = 0, kv_hi = n_k;
+  if (causal) kv_hi = min(kv_hi, q_last + delta + 1);
+  if (W >= 0) kv_lo = max(kv_lo, q0 + delta - W);
+  const int t_lo = kv_lo / kBC;
+  const int nt = kv_hi > kv_lo ? ceil_div(kv_hi, kBC) - t_lo : 0;
+
+  // this wave's rows and key range
+  const int wq0 = q0 + rblk * 32;
+  const bool wave_live = wq0 < n_q;
+  const int wq_last = min(wq0 + 31, n_q - 1);
+  int w_lo = 0, w_hi = n_k;
+  if (causal) w_hi = min(w_hi, wq_last + delta + 1);
+  if (W >= 0) w_lo = max(w_lo, wq0 + delta - W);
+  const int qi = wq0 + l32;  // this lane's query row
+
+  // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
+  // the sequence read as zeros through the descriptor bound
+  bf16x8_t qf[D / 16];
+  {
+    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // Q is in before any tile load is queued
+  }
+
+  // K/V streaming: one buffer descriptor per tensor covers a window of
+  // seg_rows key rows from seg0 (32-bit offsets); rows past the sequence end
+  // fall outside it and read as zeros.  The window moves only when a tile
+  // would cross its end, which never happens below 2^32 bytes of keys.
+  uint32_t kofs[T::kLoads], vofs[T::kLoads];
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) {
+    const int slot = (i * kWaves + wave) * 64 + lane;
+    const int r = slot / T::kKch;
+    const int ck = ((slot % T::kKch) ^ tile_swz(r)) & (T::kKch - 1);
+    const int cv = ((slot % T::kKch) ^ vtile_swz(r)) & (T::kKch - 1);
+    kofs[i] = (uint32_t)r * row_bytes + (uint32_t)ck * 16;
+    vofs[i] = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
+  }
+  int seg0 = 0, seg_end = -1;
+  u32x4_t rk = buffer_rsrc(kg, 0), rv = buffer_rsrc(vg, 0);
+  // queue the DMA of tile j (relative to t_lo) into the given slot
+  auto issue = [&](int j, char* kdst, char* vdst) {
+    const int k0 = (t_lo + j) * kBC;
+    if (k0 + kBC > seg_end) {
+      seg0 = k0;
+      seg_end = k0 + a.seg_rows;
+      const uint32_t nrec = (uint32_t)min(n_k - k0, a.seg_rows) * row_bytes;
+      rk = buffer_rsrc(kg + (long long)k0 * rs, nrec);
+      rv = buffer_rsrc(vg + (long long)k0 * rs, nrec);
+    }
+    const uint32_t base = (uint32_t)(k0 - seg0) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int blk = i * kWaves + wave;
+      dma16(rk, base + kofs[i], lds_addr(kdst + blk * 1024));
+      dma16(rv, base + vofs[i], lds_addr(vdst + blk * 1024));
+    }
+  };
+
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  float m_run = kNegInf;  // reference max of this row (base-2 scaled)
+  float l_run = 0.0f;     // partial exp-sum over this lane-half's keys (for lse)
+  float lr_run = 0.0f;    // the same over the bf16-rounded probabilities (for O)
+
+  // per-lane parts of the LDS operand addresses
+  // K rows enter in pi order (see pi_row); sub-block kb adds 32 rows.  The
+  // chunk (2 kk + half) ^ tile_swz(r) splits into the fixed low bit and
+  // (kk ^ y) in the upper bits, so fragment kk sits at k_base + ((kk << 5) ^ k_y).
+  int k_base, k_y;
+  {
+    const int r = pi_row(l32), sw = tile_swz(r);
+    k_base = r * D * 2 + ((half ^ sw) & 1) * 16;
+    k_y = ((sw >> 1) & (D / 16 - 1)) << 5;
+  }
+  // V^T fragments through the transposing read: lane j of 16-lane group g
+  // addresses row (ks*16 + 8*(g/2) + 4*u + j/4), dims db*32 + 16*(g%2) + 4*(j%4)
+  int v_off[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int r = 8 * (lg >> 1) + (j16 >> 2);
+    const int d = db * 32 + 16 * (lg & 1) + 4 * (j16 & 3);
+    v_off[db] = vtile_off<D>(r, d >> 3) + (d & 7) * 2;
+  }
+
+  f32x16_t sacc[kBC / 32];    // scores of the current tile (matrix block -> vector block)
+  bf16x8_t pf[kBC / 16];      // probabilities of the previous tile (vector block -> matrix block)
+
+  auto live = [&](int j) {
+    const int k0 = (t_lo + j) * kBC;
+    return wave_live && j >= 0 && j < nt && k0 < w_hi && k0 + kBC > w_lo;
+  };
+
+  constexpr int kPV = (kBC / 16) * (D / 32);  // P V products per tile
+  constexpr int kS = (D / 16) * (kBC / 32);   // score products per tile
+  constexpr int kLook = 4;
+  // operand of product i: V^T fragment (i < kPV) or K fragment
+  auto fetch = [&](int i, const char* kb_lds, const char* vp_lds) {
+    if (i < kPV) {
+      const int ks = i / (D / 32), db = i % (D / 32);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vp_lds + v_off[db] + ks * 16 * D * 2));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(vp_lds + v_off[db] + ks * 16 * D * 2 + 4 * D * 2));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const int kk = (i - kPV) / (kBC / 32), kb = (i - kPV) % (kBC / 32);
+    return *(const bf16x8_t*)(kb_lds + (((kk << 5) ^ k_y) + k_base) + kb * 32 * D * 2);
+  };
+  auto product = [&](int i, const bf16x8_t& f) {
+    if (i < kPV) {
+      const int ks = i / (D / 32), db = i % (D / 32);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, pf[ks], oacc[db], 0, 0, 0);
+    } else {
+      const int kk = (i - kPV) / (kBC / 32), kb = (i - kPV) % (kBC / 32);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, qf[kk], sacc[kb], 0, 0, 0);
+    }
+  };
+  // matrix block: P V of the previous tile (probabilities are zero when that
+  // tile was not live for this wave) and S of tile j; the operand fragments
+  // stream through a queue kLook products ahead of their use
+  auto mblock = [&](const char* kb_lds, const char* vp_lds) {
+    __builtin_amdgcn_s_setprio(2);  // the matrix stream wins issue arbitration on its SIMD
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+    bf16x8_t fq[kLook + 1];
+#pragma unroll
+    for (int i = 0; i < kLook; ++i) fq[i] = fetch(i, kb_lds, vp_lds);
+#pragma unroll
+    for (int i = 0; i < kPV + kS; ++i) {
+      if (i + kLook < kPV + kS) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook, kb_lds, vp_lds);
+      product(i, fq[i % (kLook + 1)]);
+    }
+    // order: the first kLook fetches, then (fetch i + kLook, product i)
+    static_assert(kPV >= kLook, "look-ahead must start inside the P V products");
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
+#pragma unroll
+    for (int i = 0; i < kPV - kLook; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kLook; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // first matrix block: S of tile 0 only
+  auto mblock_first = [&](const char* kb_lds) {
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+    for (int i = kPV; i < kPV + kS; ++i) product(i, fetch(i, kb_lds, kb_lds));
+  };
+
+  // vector block: mask, online softmax update, bf16 probabilities of tile j
+  auto vblock = [&](int j) {
+    if (!live(j)) {
+#pragma unroll
+      for (int ks = 0; ks < kBC / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)0.0f;
+      return;
+    }
+    const int k0 = (t_lo + j) * kBC;
+    const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
+                           (W >= 0 && k0 < wq_last + delta - W);
+    if (need_mask) {
+      // allowed keys of this lane's row: [lo, hi]; with e = key - lo - 8 half,
+      // a key is allowed iff both (e + c) and (hi - lo - 8 half - c) are >= 0,
+      // c being the key's constant offset in the tile; the sign bits of the
+      // two make a select mask for v_bfi (no compare results in SGPRs)
+      int hi = n_k - 1, lo = 0;
+      if (causal) hi = min(hi, qi + delta);
+      if (W >= 0) lo = max(lo, qi + delta - W);
+      const int e = k0 + 8 * half - lo, f = hi - k0 - 8 * half;
+#pragma unroll
+      for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
+          const uint32_t bad = (uint32_t)(((e + c) | (f - c)) >> 31);
+          sacc[kb][r] = __uint_as_float((bad & 0xff800000u) | (~bad & __float_as_uint(sacc[kb][r])));
+        }
+    }
+    // Probabilities against the current reference max, accepted when this
+    // lane's 32 of them sum to at most kLazyBound (so none exceeds it).
+    // Otherwise (the row's first live tile, whose reference is -inf, or a
+    // jump of the row max) take the tile's true max, rescale the state and
+    // recompute.
+    float p[kBC / 32][16];
+#pragma unroll
+    for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[kb][r] = exp2_hw(fmaf(sacc[kb][r], c2, -m_run));
+    float rsum = tree_sum<kBC / 32>(p);
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= kLazyBound)) != 0) {
+      const float m_tile = max_halves(tree_max<kBC / 32>(sacc)) * c2;
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_new == m_run ? 1.0f : exp2_hw(m_run - m_new);
+      l_run *= alpha;
+      lr_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+      const float m_use = m_run == kNegInf ? 0.0f : m_run;
+#pragma unroll
+      for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[kb][r] = exp2_hw(fmaf(sacc[kb][r], c2, -m_use));
+      rsum = tree_sum<kBC / 32>(p);
+    }
+    l_run += rsum;
+#pragma unroll
+    for (int ks = 0; ks < kBC / 16; ++ks) {
+      const int kb = ks >> 1, o8 = (ks & 1) * 8;
+      pf[ks] = to_bf16x8(p[kb][o8 + 0], p[kb][o8 + 1], p[kb][o8 + 2], p[kb][o8 + 3],
+                         p[kb][o8 + 4], p[kb][o8 + 5], p[kb][o8 + 6], p[kb][o8 + 7]);
+    }
+    // O is normalised by the sum of exactly the rounded probabilities the
+    // P V product used, so it stays a convex combination of V rows even
+    // when the dominant probability is not 1 (lazy reference)
+    lr_run += sum_rounded<kBC / 32>(p);
+  };
+
+  // Step j: tile j has landed in slot j % 4 (each wave waits for its own
+  // loads, then the barrier publishes everyone's) and the slot of tile j - 2
+  // is free to receive tile j + 2.  Group 0 runs the matrix block of step j
+  // and then the vector block of tile j; group 1 the vector block of tile
+  // j - 1 and then the matrix block of step j.  The barrier between the two
+  // halves keeps the groups half a step apart.
+  auto kslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes; };
+  auto vslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes + T::kBytes; };
+  auto land = [&](int j) {
+    if (j + 1 < nt)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::kLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    barrier();
+  };
+  // the slot of tile j - 2 is free once step j has landed; the loads are
+  // queued at the end of a vector block, where the wave would otherwise wait
+  auto prefetch = [&](int j) {
+    if (j + 2 < nt) issue(j + 2, kslot(j + 2), vslot(j + 2));
+  };
+
+  if (nt > 0) {
+    issue(0, kslot(0), vslot(0));
+    if (nt > 1) issue(1, kslot(1), vslot(1));
+    // steps 0 .. nt: step 0 has no previous tile, the last step's score
+    // product is not used
+    if (group == 0) {
+      land(0);
+      mblock_first(kslot(0));
+      barrier();
+      vblock(0);
+      prefetch(0);
+      for (int j = 1; j <= nt; ++j) {
+        land(j);
+        mblock(kslot(j), vslot(j - 1));
+        barrier();
+        vblock(j);
+        prefetch(j);
+      }
+    } else {
+      land(0);
+      prefetch(0);
+      barrier();
+      mblock_first(kslot(0));
+      for (int j = 1; j <= nt; ++j) {
+        land(j);
+        vblock(j - 1);
+        prefetch(j);
+        barrier();
+        mblock(kslot(j), vslot(j - 1));
+      }
+    }
+  }
+
+  // epilogue: O = u / l (one division per row, l over the rounded
+  // probabilities), lse = ln 2 * (m + log2 l) (l over the unrounded ones)
+  const float l_tot = sum_halves(l_run);
+  const float lr_tot = sum_halves(lr_run);
+  if (qi < n_q) {
+    const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+    uint16_t* op = og + (long long)qi * rs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + half * 4;
+        u32x2_t pr;
+        pr[0] = pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
+        pr[1] = pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
+        *(u32x2_t*)(op + d) = pr;
+      }
+    if (a.lse != nullptr && half == 0)
+      a.lse[w.lse_base + qi] = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
+  fwd_bf16_body<D, VARLEN>(a);
+}
+
+// The four-wave kernel moves its running max only when a row's new max
+// exceeds it by more than this (base-2 units): the output u / l does not
+// depend on which reference max is used, and probabilities stay <= 2^8.
+constexpr float kRescaleSlack4 = 8.0f;
+
 // Queue the DMA of K/V tile rows [k0, k0 + kBC) of one head straight into
 // LDS (no registers).  The buffer descriptor covers only the rows that exist,
 // so rows past the sequence end read as zeros without a branch.
 template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* kg, const uint16_t* vg, long long rs,
+__device__ __forceinline__ void issue_tile4(const uint16_t* kg, const uint16_t* vg, long long rs,
                                            int k0, int n_k, char* kdst, char* vdst, int wave,
                                            int lane) {
-  using T = BfTile<D>;
+  using T = BfTile<D, kQThreads>;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
   const uint32_t nrec = (uint32_t)min(n_k - k0, kBC) * row_bytes;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -187,24 +689,10 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kg, const uint16_t* v
   }
 }
 
-// Lane-half exchange on the VALU: {r0, r1} = {x[lane], x[lane ^ 32]}.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// The running max is moved only when a row's new max exceeds it by more than
-// this (base-2 units): the output u / l does not depend on which reference
-// max is used, and probabilities stay <= 2^8, far from fp32/bf16 overflow.
-constexpr float kRescaleSlack = 8.0f;
 
 template <int D, bool VARLEN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
-  using T = BfTile<D>;
+__global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
+  using T = BfTile<D, kQThreads>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char k_lds1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
@@ -215,9 +703,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   Work w;
   if constexpr (VARLEN) {
-    if (!varlen_work(a, lane, w)) return;
+    if (!varlen_work(a, kQRows, lane, w)) return;
   } else {
-    dense_work(a, ceil_div(a.seqlen_q, kBR), w);
+    dense_work(a, ceil_div(a.seqlen_q, kQRows), w);
   }
 
   const long long rs = (long long)a.heads * D;  // elements between consecutive rows
@@ -229,8 +717,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int n_q = w.n_q, n_k = w.n_k, delta = n_k - n_q;
   const int causal = a.causal, W = a.window_left;
   const float c2 = a.scale_log2;
-  const int q0 = w.qt * kBR;
-  const int q_last = min(q0 + kBR, n_q) - 1;
+  const int q0 = w.qt * kQRows;
+  const int q_last = min(q0 + kQRows, n_q) - 1;
 
   // K/V tiles this query tile needs (fully masked ones are skipped)
   int kv_lo = 0, kv_hi = n_k;
@@ -332,7 +820,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     const float m_tile = max_halves(mx) * c2;
-    const bool grow = m_tile > m_run + kRescaleSlack;
+    const bool grow = m_tile > m_run + kRescaleSlack4;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? m_tile : m_run;
       const float alpha = grow ? exp2_hw(m_run - m_new) : 1.0f;
@@ -375,17 +863,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   if (t_lo < t_hi) {
-    issue_tile<D>(kg, vg, rs, t_lo * kBC, n_k, k_lds0, v_lds0, wave, lane);
+    issue_tile4<D>(kg, vg, rs, t_lo * kBC, n_k, k_lds0, v_lds0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile t_lo are in
     __syncthreads();
     // two tiles per trip so that each buffer is a distinct LDS object
     for (int kt = t_lo; kt < t_hi; kt += 2) {
-      if (kt + 1 < t_hi) issue_tile<D>(kg, vg, rs, (kt + 1) * kBC, n_k, k_lds1, v_lds1, wave, lane);
+      if (kt + 1 < t_hi) issue_tile4<D>(kg, vg, rs, (kt + 1) * kBC, n_k, k_lds1, v_lds1, wave, lane);
       compute_tile(kt, k_lds0, v_lds0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       if (kt + 1 < t_hi) {
-        if (kt + 2 < t_hi) issue_tile<D>(kg, vg, rs, (kt + 2) * kBC, n_k, k_lds0, v_lds0, wave, lane);
+        if (kt + 2 < t_hi) issue_tile4<D>(kg, vg, rs, (kt + 2) * kBC, n_k, k_lds0, v_lds0, wave, lane);
         compute_tile(kt + 1, k_lds1, v_lds1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
@@ -413,15 +901,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 variant: same tiling and update, fp32 operands on
-// v_mfma_f32_32x32x2f32 (exact fp32 products), probabilities kept in fp32.
-// Single-buffered 32-key tiles; dense only.
 
-constexpr int kBC32 = 32;
+// ---------------------------------------------------------------------------
+// fp32 variant: same update, fp32 operands on v_mfma_f32_32x32x2f32 (exact
+// fp32 products), probabilities kept in fp32.  4 waves x 32 query rows,
+// single-buffered 32-key tiles; dense only.
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads32, 2) void fwd_fp32_kernel(FwdArgs a) {
   constexpr int kStride = D + 1;  // padded LDS row (floats) -> conflict-free column reads
   __shared__ float ks_lds[kBC32 * kStride];
   __shared__ float vs_lds[kBC32 * D];
@@ -429,7 +916,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
 
   Work w;
-  dense_work(a, ceil_div(a.seqlen_q, kBR), w);
+  dense_work(a, ceil_div(a.seqlen_q, kBR32), w);
   const long long rs = (long long)a.heads * D;
   const float* qg = (const float*)a.q + (w.q_row0 * a.heads + w.h) * D;
   const float* kg = (const float*)a.k + (w.k_row0 * a.heads + w.h) * D;
@@ -439,8 +926,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
   const int n_q = w.n_q, n_k = w.n_k, delta = n_k - n_q;
   const int causal = a.causal, W = a.window_left;
   const float c2 = a.scale_log2;
-  const int q0 = w.qt * kBR;
-  const int q_last = min(q0 + kBR, n_q) - 1;
+  const int q0 = w.qt * kBR32;
+  const int q_last = min(q0 + kBR32, n_q) - 1;
   int kv_lo = 0, kv_hi = n_k;
   if (causal) kv_hi = min(kv_hi, q_last + delta + 1);
   if (W >= 0) kv_lo = max(kv_lo, q0 + delta - W);
@@ -474,7 +961,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
   for (int kt = t_lo; kt < t_hi; ++kt) {
     const int k0 = kt * kBC32;
     __syncthreads();  // previous tile fully consumed
-    for (int e = tid; e < kBC32 * D; e += kThreads) {
+    for (int e = tid; e < kBC32 * D; e += kThreads32) {
       const int r = e / D, c = e % D;
       const int key = k0 + r;
       const bool ok = key < n_k;
@@ -558,24 +1045,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp32_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool VARLEN>
-hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t stream) {
+template <bool VARLEN>
+hipError_t launch_bf16_d128(const FwdArgs& a, hipStream_t stream) {
   const int nqt = ceil_div(a.seqlen_q, kBR);
   const long long grid = (long long)a.batch * a.heads * nqt;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<128, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t launch_bf16_d64(const FwdArgs& a, hipStream_t stream) {
+  const int nqt = ceil_div(a.seqlen_q, kQRows);
+  const long long grid = (long long)a.batch * a.heads * nqt;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_bf16_q_kernel<64, VARLEN>), dim3((unsigned)grid), dim3(kQThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fp32_t(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = ceil_div(a.seqlen_q, kBR);
+  const int nqt = ceil_div(a.seqlen_q, kBR32);
   const long long grid = (long long)a.batch * a.heads * nqt;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fwd_fp32_kernel<D>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(fwd_fp32_kernel<D>, dim3((unsigned)grid), dim3(kThreads32), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -583,8 +1081,8 @@ hipError_t launch_fp32_t(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream) {
   const bool varlen = a.cu_q != nullptr;
-  if (d == 128) return varlen ? launch_bf16_t<128, true>(a, stream) : launch_bf16_t<128, false>(a, stream);
-  if (d == 64) return varlen ? launch_bf16_t<64, true>(a, stream) : launch_bf16_t<64, false>(a, stream);
+  if (d == 128) return varlen ? launch_bf16_d128<true>(a, stream) : launch_bf16_d128<false>(a, stream);
+  if (d == 64) return varlen ? launch_bf16_d64<true>(a, stream) : launch_bf16_d64<false>(a, stream);
   return hipErrorInvalidValue;
 }
 
