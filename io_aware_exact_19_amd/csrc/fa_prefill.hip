@@ -271,22 +271,17 @@ __device__ __forceinline__ float tree_max(const f32x16_t (&v)[N]) {
   return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
 }
 
-// Sum of the bf16-rounded values of N x 16 floats: pairs rounded to bf16
-// (the same rounding as the P V operand) and summed by dot products with
-// (1, 1) accumulated in fp32.
+// acc + the sum of 8 bf16 values (dot products with (1, 1) in fp32).  The
+// pairs are extracted as bf16x2 halves of the vector itself.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-template <int N>
-__device__ __forceinline__ float sum_rounded(const float (&v)[N][16]) {
+__device__ __forceinline__ float sum_rounded_pairs(const bf16x8_t& v, float acc) {
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int n = 0; n < N; ++n)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16x2_t pr = {(__bf16)v[n][2 * i], (__bf16)v[n][2 * i + 1]};
-      a[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, a[i & 3], false);
-    }
-  return (a[0] + a[1]) + (a[2] + a[3]);
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2_t pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
 }
 
 // s_waitcnt immediates: wait until at most n vector-memory operations are
@@ -471,11 +466,18 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
     bf16x8_t fq[kLook + 1];
 #pragma unroll
     for (int i = 0; i < kLook; ++i) fq[i] = fetch(i, kb_lds, vp_lds);
+    // O is normalised by the sum of exactly the rounded probabilities the
+    // P V product uses (a convex combination of V rows even when the
+    // dominant probability is not 1 under the lazy reference); the dot
+    // products run here, beside the matrix stream, not in the vector block
+    float ra[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < kPV + kS; ++i) {
       if (i + kLook < kPV + kS) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook, kb_lds, vp_lds);
       product(i, fq[i % (kLook + 1)]);
+      if (i < kBC / 16) ra[i & 3] = sum_rounded_pairs(pf[i], ra[i & 3]);
     }
+    lr_run += (ra[0] + ra[1]) + (ra[2] + ra[3]);
     // order: the first kLook fetches, then (fetch i + kLook, product i)
     static_assert(kPV >= kLook, "look-ahead must start inside the P V products");
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
@@ -569,10 +571,6 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       pf[ks] = to_bf16x8(p[kb][o8 + 0], p[kb][o8 + 1], p[kb][o8 + 2], p[kb][o8 + 3],
                          p[kb][o8 + 4], p[kb][o8 + 5], p[kb][o8 + 6], p[kb][o8 + 7]);
     }
-    // O is normalised by the sum of exactly the rounded probabilities the
-    // P V product used, so it stays a convex combination of V rows even
-    // when the dominant probability is not 1 (lazy reference)
-    lr_run += sum_rounded<kBC / 32>(p);
   };
 
   // Step j: tile j has landed in slot j % 4 (each wave waits for its own
