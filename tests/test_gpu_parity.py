@@ -61,6 +61,13 @@ SMALL_BF16 = [
     (1, 2, 130, 130, 128, False, 7),   # window without causal
     (3, 1, 129, 64, 64, False, -1),
     (1, 2, 1, 700, 128, True, -1),     # one query at the end of 700 keys
+    # d = 128 runs the two-group kernel (256 query rows per workgroup)
+    (1, 2, 700, 700, 128, True, 100),  # window: first needed tile > 0, several workgroups
+    (1, 2, 333, 200, 128, True, -1),   # n_q > n_k: rows without keys, dead waves
+    (2, 2, 600, 600, 128, False, 150), # window without causal, several tiles
+    (1, 3, 1000, 1000, 128, True, 1024),  # window wider than the sequence
+    (1, 1, 257, 257, 128, True, 31),   # window narrower than a tile
+    (1, 1, 513, 1100, 128, False, -1), # n_q just past two workgroups, ragged keys
 ]
 
 
@@ -169,6 +176,74 @@ def test_varlen_small():
     _varlen_case([5, 1, 300, 129, 64, 0, 200], 2, 64, True, 50, seed=31)
     _varlen_case([130, 70, 257], 3, 128, False, -1, seed=32)
     _varlen_case([1000, 17, 513], 2, 128, True, -1, seed=33)
+    _varlen_case([0, 1, 2, 300, 700, 5, 256, 257], 2, 128, True, 64, seed=35)
+
+
+def _scaled_case(q, k, v, causal, W, what):
+    """Dense bf16 case on given CPU inputs, checked element by element."""
+    d = q.shape[-1]
+    s = 1.0 / math.sqrt(d)
+    announce(what)
+    o, lse = fa.attention(q.cuda(), k.cuda(), v.cuda(), scale=s, causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_dense(_np(q), _np(k), _np(v), s, causal, W)
+    check(o.cpu(), lse.cpu(), o_ref, lse_ref, torch.bfloat16, what)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_growing_scores_rescale_repeatedly(d):
+    """Scores rise along the keys (K row j carries j times a direction that Q
+    points along), so the row maximum grows from tile to tile and the lazy
+    reference must move many times; the output is dominated by the last
+    allowed keys."""
+    B, H, N = 1, 2, 900
+    q, k, v = inputs.dense_qkv(B, N, N, H, d, 61)
+    ramp = torch.linspace(0.0, 400.0, N).view(1, N, 1, 1)
+    k = (k.float() * 0.05 + ramp * torch.ones(d) / math.sqrt(d) * 0.5).to(torch.bfloat16)
+    q = (q.float() * 0.05 + torch.ones(d) / math.sqrt(d) * 4.0).to(torch.bfloat16)
+    for causal in (False, True):
+        _scaled_case(q, k, v, causal, -1, f"growing scores d{d} causal{int(causal)}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_extreme_score_magnitudes(d):
+    """Scores of several hundred in natural units (exp would overflow fp32
+    without the reference shift), with the maximum placed in a late tile."""
+    B, H, N = 1, 2, 600
+    q, k, v = inputs.dense_qkv(B, N, N, H, d, 62)
+    q = (q.float() * 16.0).to(torch.bfloat16)
+    k = (k.float() * 16.0).to(torch.bfloat16)
+    _scaled_case(q, k, v, False, -1, f"extreme scores d{d}")
+    _scaled_case(q, k, v, True, 200, f"extreme scores d{d} causal window")
+
+
+def test_key_range_beyond_one_buffer_window():
+    """More than 2^32 bytes of keys for one head at a head stride of 16 KiB
+    (64 heads x d 128): the d = 128 kernel addresses K/V through buffer
+    windows of at most 2^32 bytes and must move its window part-way through
+    the keys.  4.3 GB each for K and V, generated on the device; sampled
+    (row, head) outputs checked against the oracle."""
+    H, d, n_q = 64, 128, 64
+    win = (2 ** 32 - 1) // (H * d * 2) // 64 * 64   # keys per window
+    n_k = win + 1000
+    dev = "cuda"
+    announce(f"dense n_q {n_q} n_k {n_k} H{H} d{d} (window {win} keys)")
+    q = inputs.normal((1, n_q, H, d), 71, device=dev)
+    k = inputs.normal((1, n_k, H, d), 72, device=dev)
+    v = inputs.normal((1, n_k, H, d), 73, device=dev)
+    s = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        o, lse = fa.attention(q, k, v, scale=s, causal=causal)
+        torch.cuda.synchronize()
+        for h in (0, 37, 63):
+            kh, vh = _np(k[0, :, h].cpu()), _np(v[0, :, h].cpu())
+            rows = np.array([0, 31, 63])
+            o_ref, lse_ref = oracle.sdpa(_np(q[0, rows, h].cpu()), kh, vh, s, causal,
+                                         q_index=rows, n_q=n_q)
+            check(o[0, rows, h].cpu(), lse[0, h, rows].cpu(), o_ref, lse_ref, torch.bfloat16,
+                  f"window crossing causal{int(causal)} head {h}")
+    del q, k, v
+    torch.cuda.empty_cache()
 
 
 def test_varlen_equals_per_sequence_dense():
