@@ -115,6 +115,8 @@ size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int ch
  * whole chunk states).  d: 64 or 128.  workspace_bytes must be at least
  * fa_decode_workspace_size(batch, heads, max_len, d, chunk).
  * L_b == 0 gives O = 0 and lse = -inf for that sequence.
+ * FA_ERR_UNSUPPORTED also when one chunk of cache rows spans 2 GiB or more
+ * (chunk * heads * d * 2 bytes) or batch * heads * chunks exceeds 2^31 - 1.
  */
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
               void* o, float* lse, int batch, int heads, int max_len, int d, float scale,

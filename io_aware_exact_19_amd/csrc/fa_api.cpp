@@ -107,6 +107,7 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     return FA_ERR_WORKSPACE;
   const int max_chunks = (max_len + chunk - 1) / chunk;
   if ((long long)batch * heads * max_chunks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
+  if ((long long)chunk * heads * d * 2 >= 0x80000000LL) return FA_ERR_UNSUPPORTED;
 
   fa::DecodeArgs a;
   a.q = q;

@@ -120,6 +120,8 @@ def _dec(**kw):
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
     (dict(chunk=0), fa.FA_ERR_INVALID_ARG),
+    # one 512-key chunk of 16384 heads x 128 dims spans 2 GiB of cache rows
+    (dict(batch=1, heads=16384, max_len=512, chunk=512), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(workspace=0), fa.FA_ERR_WORKSPACE),
     (dict(workspace_bytes=16), fa.FA_ERR_WORKSPACE),

@@ -306,6 +306,13 @@ def test_decode_small(d, chunk):
     _decode_case(3, 2, 1000, d, [1, 257, 1000], chunk, seed=41)
 
 
+@pytest.mark.parametrize("H,d,chunk", [(3, 128, 256), (20, 128, 128), (40, 64, 64), (33, 64, 512)])
+def test_decode_ragged_heads(H, d, chunk):
+    """Head counts that leave the last head group of a workgroup partly
+    empty; lengths on, just before and just after chunk and step edges."""
+    _decode_case(4, H, 1030, d, [16, 511, 1030, 513], chunk, seed=44)
+
+
 def test_decode_empty_sequence():
     q, o, lse = _decode_case(2, 2, 64, 128, [0, 5], 64, seed=42, pairs=[(1, 0), (1, 1)])
     assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
