@@ -92,12 +92,27 @@ struct Work {
 };
 
 __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
-  const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int bh = id / nqt;
-  const int t = id - bh * nqt;
+  const int nbh = a.batch * a.heads;
+  int bh, t;  // t: rank of the tile in start order, 0 = started first
+  if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
+    // Tiles differ in length.  Workgroup i goes to XCD i % 8, which starts
+    // its workgroups in order as CUs free up: give XCD x the heads
+    // [x*hx, (x+1)*hx) and let it start all their tiles longest first, so
+    // the short tiles fill in behind the long ones (longest-processing-time
+    // order); each head's tiles stay on one XCD and share its L2.
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3, hx = nbh >> 3;
+    t = k / hx;
+    bh = x * hx + (k - t * hx);
+  } else {
+    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = id / nqt;
+    t = id - bh * nqt;
+  }
   const int b = bh / a.heads;
   w.h = bh - b * a.heads;
-  w.qt = nqt - 1 - t;  // longest (causal) tiles first
+  // causal: later tiles see more keys; a left window without the causal
+  // bound: earlier tiles see more keys
+  w.qt = a.causal || a.window_left < 0 ? nqt - 1 - t : t;
   w.n_q = a.seqlen_q;
   w.n_k = a.seqlen_k;
   w.q_row0 = (long long)b * a.seqlen_q;
@@ -341,22 +356,6 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   if (W >= 0) w_lo = max(w_lo, wq0 + delta - W);
   const int qi = wq0 + l32;  // this lane's query row
 
-  // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
-  // the sequence read as zeros through the descriptor bound
-  bf16x8_t qf[D / 16];
-  {
-    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
-          rq, (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2, 0, 0);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, x);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // Q is in before any tile load is queued
-  }
-
   // K/V streaming: one buffer descriptor per tensor covers a window of
   // seg_rows key rows from seg0 (32-bit offsets); rows past the sequence end
   // fall outside it and read as zeros.  The window moves only when a tile
@@ -391,6 +390,30 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       dma16(rv, base + vofs[i], lds_addr(vdst + blk * 1024));
     }
   };
+
+  auto kslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes; };
+  auto vslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes + T::kBytes; };
+  if (nt > 0) {
+    issue(0, kslot(0), vslot(0));
+    if (nt > 1) issue(1, kslot(1), vslot(1));
+  }
+
+  // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
+  // the sequence read as zeros through the descriptor bound
+  bf16x8_t qf[D / 16];
+  {
+    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2, 0, 0);
+      qf[kk] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    // Q and the first two tiles are in flight together; the wait covers all
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
 
   f32x16_t oacc[D / 32];
 #pragma unroll
@@ -579,8 +602,6 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   // and then the vector block of tile j; group 1 the vector block of tile
   // j - 1 and then the matrix block of step j.  The barrier between the two
   // halves keeps the groups half a step apart.
-  auto kslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes; };
-  auto vslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes + T::kBytes; };
   auto land = [&](int j) {
     if (j + 1 < nt)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * T::kLoads));
@@ -595,8 +616,6 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   };
 
   if (nt > 0) {
-    issue(0, kslot(0), vslot(0));
-    if (nt > 1) issue(1, kslot(1), vslot(1));
     // steps 0 .. nt: step 0 has no previous tile, the last step's score
     // product is not used
     if (group == 0) {
