@@ -18,6 +18,9 @@ timed steps.  The line also carries:
   packed varlen with a 1024-key window, fp32 small case, and KV-cache decode
   in HBM GB/s with its own roofline), each timed the same way.
 
+Every workload first runs back to back for ``--settle-ms`` (default 400 ms)
+so that the engine clock has left its idle ramp before the warmup steps.
+
 ``--profile-target NAME`` runs only NAME's launches (plus, with
 ``--calibrate-copy``, a plain device copy of known size) for rocprofv3.
 ``--pmc-summary FETCH_DIR WRITE_DIR`` turns two ``rocprofv3 --pmc`` runs into
@@ -163,9 +166,29 @@ def make_decode(torch, fa, inputs, configs, cfg):
 # ---------------------------------------------------------------- timing
 
 
-def time_launches(torch, w, steps, warmup):
-    """Warm up, then time exactly ``steps`` launches: wall clock between two
-    device synchronisations, and per-launch HIP events on the launch stream."""
+def settle(torch, w, ms):
+    """Launch the workload back to back for ``ms`` milliseconds of wall time.
+
+    The engine clock of an idle GPU ramps up over the first few tens of
+    milliseconds of sustained load (measured: the first 40 launches of the
+    headline workload ran ~15 % slower than launches 50 ms later), so a short
+    warmup alone would time the ramp, not the kernel."""
+    t_end = time.perf_counter() + ms * 1e-3
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            w.launch()
+        torch.cuda.synchronize()
+        n += 4
+    return n
+
+
+def time_launches(torch, w, steps, warmup, settle_ms=0.0):
+    """Let the clock settle, warm up, then time exactly ``steps`` launches:
+    wall clock between two device synchronisations, and per-launch HIP events
+    on the launch stream."""
+    if settle_ms > 0:
+        settle(torch, w, settle_ms)
     for _ in range(warmup):
         w.launch()
     torch.cuda.synchronize()
@@ -316,6 +339,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="back-to-back launches before the warmup steps (engine clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-target", default=None,
@@ -366,7 +391,7 @@ def main():
 
     if args.profile_target:
         w = builders[args.profile_target]()
-        wall, mean_ms, min_ms = time_launches(torch, w, args.steps, args.warmup)
+        wall, mean_ms, min_ms = time_launches(torch, w, args.steps, args.warmup, args.settle_ms)
         log(f"[profile] {w.name}: {args.steps} launches, mean {mean_ms:.4f} ms, "
             f"{rate(w, mean_ms):.2f} {w.unit}")
         if args.calibrate_copy:
@@ -381,8 +406,9 @@ def main():
 
     # ---- headline: B4 H16 N2048 d128 bf16 non-causal prefill
     head = builders["prefill_2k"]()
-    log(f"[bench] timing {head.name}: warmup {args.warmup}, steps {args.steps}")
-    wall_ms, mean_ms, min_ms = time_launches(torch, head, args.steps, args.warmup)
+    log(f"[bench] timing {head.name}: settle {args.settle_ms:.0f} ms, warmup {args.warmup}, "
+        f"steps {args.steps}")
+    wall_ms, mean_ms, min_ms = time_launches(torch, head, args.steps, args.warmup, args.settle_ms)
     achieved = rate(head, mean_ms)
     traffic = read_traffic(TRAFFIC_SUMMARY, PREFILL_KERNEL_SRC)
     result = {
@@ -398,7 +424,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: i.i.d. N(0,1) bf16 Q/K/V from fixed seeds, inputs resident in HBM",
-        "config": head.config,
+        "config": dict(head.config, settle_ms=args.settle_ms),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
@@ -422,7 +448,7 @@ def main():
             w = builders[key]()
             steps = 20 if key != "decode" else 10
             log(f"[bench] timing {w.name}")
-            wall, mean2, min2 = time_launches(torch, w, steps, 3)
+            wall, mean2, min2 = time_launches(torch, w, steps, 3, args.settle_ms)
             r = rate(w, mean2)
             entry = {"workload": w.name, "value": round(r, 3), "unit": w.unit,
                      "frac_of_peak": round(r / w.peak, 4), "peak": w.peak, "bound": w.bound,

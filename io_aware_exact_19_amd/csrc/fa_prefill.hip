@@ -527,6 +527,18 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
 #pragma unroll
     for (int i = kPV; i < kPV + kS; ++i) product(i, fetch(i, kb_lds, kb_lds));
   };
+  // last matrix block: P V of the last tile only (there is no next tile to score)
+  auto mblock_last = [&](const char* vp_lds) {
+    __builtin_amdgcn_s_setprio(2);
+    float ra[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kPV; ++i) {
+      product(i, fetch(i, vp_lds, vp_lds));
+      if (i < kBC / 16) ra[i & 3] = sum_rounded_pairs(pf[i], ra[i & 3]);
+    }
+    lr_run += (ra[0] + ra[1]) + (ra[2] + ra[3]);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
   // vector block: mask, online softmax update, bf16 probabilities of tile j
   auto vblock = [&](int j) {
@@ -616,33 +628,39 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   };
 
   if (nt > 0) {
-    // steps 0 .. nt: step 0 has no previous tile, the last step's score
-    // product is not used
+    // steps 0 .. nt: step 0 has no previous tile, step nt no next one
     if (group == 0) {
       land(0);
       mblock_first(kslot(0));
       barrier();
       vblock(0);
       prefetch(0);
-      for (int j = 1; j <= nt; ++j) {
+      for (int j = 1; j < nt; ++j) {
         land(j);
         mblock(kslot(j), vslot(j - 1));
         barrier();
         vblock(j);
         prefetch(j);
       }
+      land(nt);
+      mblock_last(vslot(nt - 1));
+      barrier();  // pairs with group 1's barrier before its last matrix block
     } else {
       land(0);
       prefetch(0);
       barrier();
       mblock_first(kslot(0));
-      for (int j = 1; j <= nt; ++j) {
+      for (int j = 1; j < nt; ++j) {
         land(j);
         vblock(j - 1);
         prefetch(j);
         barrier();
         mblock(kslot(j), vslot(j - 1));
       }
+      land(nt);
+      vblock(nt - 1);
+      barrier();
+      mblock_last(vslot(nt - 1));
     }
   }
 
