@@ -455,6 +455,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   constexpr int kPV = (kBC / 16) * (D / 32);  // P V products per tile
   constexpr int kS = (D / 16) * (kBC / 32);   // score products per tile
   constexpr int kLook = 4;
+  // issue order of the matrix block: P V and score products alternate, so
+  // each accumulator chain has several independent products between its
+  // own (the score chains are only kBC/32 deep)
+  auto op = [&](int i) { return (i & 1) ? kPV + (i >> 1) : (i >> 1); };
+  static_assert(kPV == kS, "alternating order needs equal product counts");
   // operand of product i: V^T fragment (i < kPV) or K fragment
   auto fetch = [&](int i, const char* kb_lds, const char* vp_lds) {
     if (i < kPV) {
@@ -488,7 +493,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
     bf16x8_t fq[kLook + 1];
 #pragma unroll
-    for (int i = 0; i < kLook; ++i) fq[i] = fetch(i, kb_lds, vp_lds);
+    for (int i = 0; i < kLook; ++i) fq[i] = fetch(op(i), kb_lds, vp_lds);
     // O is normalised by the sum of exactly the rounded probabilities the
     // P V product uses (a convex combination of V rows even when the
     // dominant probability is not 1 under the lazy reference); the dot
@@ -496,21 +501,19 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
     float ra[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < kPV + kS; ++i) {
-      if (i + kLook < kPV + kS) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook, kb_lds, vp_lds);
-      product(i, fq[i % (kLook + 1)]);
+      if (i + kLook < kPV + kS) fq[(i + kLook) % (kLook + 1)] = fetch(op(i + kLook), kb_lds, vp_lds);
+      product(op(i), fq[i % (kLook + 1)]);
       if (i < kBC / 16) ra[i & 3] = sum_rounded_pairs(pf[i], ra[i & 3]);
     }
     lr_run += (ra[0] + ra[1]) + (ra[2] + ra[3]);
-    // order: the first kLook fetches, then (fetch i + kLook, product i)
-    static_assert(kPV >= kLook, "look-ahead must start inside the P V products");
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kLook, 0);
+    // order: the first kLook fetches, then (fetch i + kLook, product i); a P V
+    // operand takes two LDS reads, a score operand one
+    static_assert(kLook % 2 == 0, "slot parity of look-ahead fetches");
+    __builtin_amdgcn_sched_group_barrier(0x100, 3 * kLook / 2, 0);
 #pragma unroll
-    for (int i = 0; i < kPV - kLook; ++i) {
+    for (int i = 0; i < (kPV + kS - kLook) / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
