@@ -15,8 +15,9 @@ timed steps.  The line also carries:
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host's cores on the
   same workload;
 * ``secondary``: the other workloads (causal 2k, 8000-token causal prompt,
-  packed varlen with a 1024-key window, fp32 small case, and KV-cache decode
-  in HBM GB/s with its own roofline), each timed the same way.
+  packed varlen with a 1024-key window, fp32 small case, KV-cache decode in
+  HBM GB/s, and chunked prefill of 512 new tokens against KV caches), each
+  timed the same way.
 
 Every workload first runs back to back for ``--settle-ms`` (default 400 ms)
 so that the engine clock has left its idle ramp before the warmup steps.
@@ -159,6 +160,35 @@ def make_decode(torch, fa, inputs, configs, cfg):
     conf = dict(workload=cfg["name"], batch=B, heads=H, d=d, max_len=L, chunk=chunk,
                 kv_rows=int(lens.sum()), kv_bytes=kv_bytes)
     w = Workload(cfg["name"], launch, byts, "GB/s", PEAK_HBM_GBS, "hbm", "bf16", conf)
+    w.tensors = (kc, vc)
+    return w
+
+
+def make_kvcache(torch, fa, inputs, configs, cfg):
+    """Chunked prefill: n_new new tokens per sequence against its KV cache."""
+    B, H, d, L, n = cfg["batch"], cfg["heads"], cfg["d"], cfg["max_len"], cfg["n_new"]
+    lens = inputs.lengths(B, cfg["len_lo"], cfg["len_hi"], cfg["seed"]).to(torch.int32)
+    kc = inputs.decode_cache(B, L, H, d, lens, cfg["seed"], "cuda", "k")
+    vc = inputs.decode_cache(B, L, H, d, lens, cfg["seed"], "cuda", "v")
+    q = inputs.normal((B, n, H, d), inputs.subseed(cfg["seed"], "q")).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device="cuda")
+    sl = lens.cuda()
+    s = configs.default_scale(d)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fa.fa_fwd_kvcache(q, kc, vc, sl, o, lse, B, H, n, L, d, s, int(cfg["causal"]), -1,
+                               stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_kvcache")
+
+    # allowed pairs: query i of sequence b sees keys 0 .. L_b - n + i (bottom-right causal)
+    pairs = sum(n * (int(Lb) - n) + n * (n + 1) // 2 for Lb in lens.tolist())
+    conf = dict(workload=cfg["name"], batch=B, heads=H, d=d, n_new=n, max_len=L,
+                lengths=[int(x) for x in lens.tolist()])
+    w = Workload(cfg["name"], launch, 4 * d * H * pairs, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma",
+                 "bf16", conf)
     w.tensors = (kc, vc)
     return w
 
@@ -345,7 +375,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-target", default=None,
                     choices=["prefill_2k", "prefill_2k_causal", "long_8k", "varlen", "small_fp32",
-                             "decode"])
+                             "decode", "kvcache"])
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-target", default="prefill_2k")
@@ -387,6 +417,7 @@ def main():
         "small_fp32": lambda: make_dense(torch, fa, inputs, configs, configs.SMALL_FP32,
                                          dtype_name="f32"),
         "decode": lambda: make_decode(torch, fa, inputs, configs, configs.DECODE),
+        "kvcache": lambda: make_kvcache(torch, fa, inputs, configs, configs.KVCACHE),
     }
 
     if args.profile_target:
@@ -444,7 +475,7 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode"):
+        for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode", "kvcache"):
             w = builders[key]()
             steps = 20 if key != "decode" else 10
             log(f"[bench] timing {w.name}")
@@ -457,7 +488,7 @@ def main():
             if key == "decode":
                 entry["kv_bytes_per_launch"] = w.config["kv_bytes"]
                 entry["traffic"] = read_traffic(DECODE_TRAFFIC_SUMMARY, DECODE_KERNEL_SRC)
-            if key == "varlen":
+            if key in ("varlen", "kvcache"):
                 entry["lengths"] = w.config["lengths"]
             sec.append(entry)
             log(f"[bench] {w.name}: {r:.2f} {w.unit} ({100 * r / w.peak:.1f}% of peak)")

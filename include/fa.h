@@ -92,6 +92,31 @@ int fa_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse
                 const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream);
 
 /*
+ * fa_fwd_kvcache -- several new query tokens per sequence (chunked prefill,
+ * multi-token decode) against a KV cache that already holds them, bf16.
+ * The pages list inference against cached keys/values among the interfaces
+ * ("FlashAttention" (aiwiki.page), section "Software integration and
+ * limitations"); the queries are the last seqlen_q positions of each
+ * sequence, so causal masking is bottom-right aligned (delta = L_b - seqlen_q).
+ *   q, o:             [batch, seqlen_q, heads, d] bf16;
+ *   k_cache, v_cache: [batch, max_len, heads, d] bf16;
+ *   seqlens_k:        device int32 [batch], L_b = keys of sequence b (rows
+ *                     0 .. L_b-1 of its cache block, the new tokens last);
+ *                     precondition 0 <= L_b <= max_len (reads are clamped to
+ *                     the block).  Rows L_b .. max_len-1 are never read.
+ *   lse:              [batch, heads, seqlen_q] fp32 or NULL.
+ * d: 64 or 128.  causal, window_left: as for fa_fwd, relative to the
+ * bottom-right diagonal; a query with no allowed key gets O = 0, lse = -inf.
+ * The same kernels as dense fa_fwd serve it (query tiles of 256 rows at
+ * d = 128, 128 at d = 64), so small seqlen_q leaves most of a tile idle;
+ * seqlen_q == 1 is better served by fa_decode.
+ */
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                   const int* seqlens_k, void* o, float* lse, int batch, int heads,
+                   int seqlen_q, int max_len, int d, float scale, int causal,
+                   int window_left, void* stream);
+
+/*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
  * per (batch, head, chunk) an fp32 partial output of d values and one fp32
  * partial log-sum-exp, chunks = ceil(max_len / chunk).  Returns 0 for

@@ -13,12 +13,14 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     FAError,
     attention,
+    attention_kvcache,
     attention_varlen,
     decode,
     fa_decode,
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_fp32,
+    fa_fwd_kvcache,
     fa_status_string,
     load_library,
 )

@@ -29,7 +29,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_decode_workspace_size", "fa_decode", "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_decode_workspace_size", "fa_decode",
+            "fa_status_string")
 
 _lib = None
 
@@ -56,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = I
     lib.fa_fwd_fp32.argtypes = fwd_args
     lib.fa_fwd_fp32.restype = I
+    lib.fa_fwd_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.fa_fwd_kvcache.restype = I
     lib.fa_decode_workspace_size.argtypes = [I, I, I, I, I]
     lib.fa_decode_workspace_size.restype = Z
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
@@ -98,6 +101,13 @@ def fa_fwd_fp32(q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, d, scale, cau
                                       heads, seqlen_q, seqlen_k, d, scale, int(causal),
                                       window_left, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                       _stream(stream))
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, seqlen_q, max_len, d,
+                   scale, causal, window_left, stream=None) -> int:
+    return load_library().fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k),
+                                         _ptr(o), _ptr(lse), batch, heads, seqlen_q, max_len, d,
+                                         scale, int(causal), window_left, _stream(stream))
 
 
 def fa_decode_workspace_size(batch, heads, max_len, d, chunk) -> int:
@@ -182,6 +192,30 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seql
                 int(causal), int(window_left), cu_seqlens_q, cu_seqlens_k, stream)
     if st != FA_OK:
         raise FAError(st, "fa_fwd (varlen)")
+    return o, lse
+
+
+def attention_kvcache(q, k_cache, v_cache, seqlens_k, *, scale=None, causal=True, window_left=-1,
+                      return_lse=True, out=None, stream=None):
+    """q [B, n_new, H, d] (the last n_new positions of each sequence), caches
+    [B, max_len, H, d] bf16 holding them, seqlens_k int32 [B] on the GPU.
+    Returns (o [B, n_new, H, d], lse [B, H, n_new])."""
+    _check_tensor("q", q, torch.bfloat16, 4)
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4)
+    _check_tensor("seqlens_k", seqlens_k, torch.int32, 1)
+    B, n_new, H, d = q.shape
+    if k_cache.shape[0] != B or k_cache.shape[2] != H or k_cache.shape[3] != d:
+        raise ValueError("cache shape mismatch")
+    if v_cache.shape != k_cache.shape or seqlens_k.numel() != B:
+        raise ValueError("cache/seqlens shape mismatch")
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, n_new), dtype=torch.float32, device=q.device) if return_lse else None
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, B, H, n_new, k_cache.shape[1], d,
+                        s, int(causal), int(window_left), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache")
     return o, lse
 
 

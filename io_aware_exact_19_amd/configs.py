@@ -28,6 +28,13 @@ DECODE = dict(name="decode_bf16_b64_h32_len1024to32768_d128_chunk256", kind="dec
 
 ALL = [SMALL_FP32, PREFILL_2K, LONG_8K, VARLEN, DECODE]
 
+# Chunked prefill against a KV cache (several new tokens per sequence): a
+# synthetic workload of the next step after single-token decode, not one of
+# the five configurations above.
+KVCACHE = dict(name="kvcache_bf16_b8_h32_new512_len1024to16384_d128_causal", kind="kvcache",
+               dtype="bf16", batch=8, heads=32, n_new=512, len_lo=1024, len_hi=16384,
+               max_len=16384, d=128, causal=True, seed=66)
+
 
 def default_scale(d: int) -> float:
     """1 / sqrt(d), the scale of the attention definition."""

@@ -13,7 +13,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, float* lse,
                int batch, int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
-               int window_left, const int* cu_q, const int* cu_k, void* stream) {
+               int window_left, const int* cu_q, const int* cu_k, void* stream,
+               const int* seqlens_k = nullptr) {
   if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
   if (d <= 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
@@ -30,6 +31,7 @@ int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, 
     return FA_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
   if (cu_q != nullptr && (!aligned(cu_q, 4) || !aligned(cu_k, 4))) return FA_ERR_INVALID_ARG;
+  if (seqlens_k != nullptr && !aligned(seqlens_k, 4)) return FA_ERR_INVALID_ARG;
   // the grid has batch * heads * ceil(seqlen_q / 128) workgroups
   const long long grid = (long long)batch * heads * ((seqlen_q + 127) / 128);
   if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
@@ -56,6 +58,8 @@ int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, 
   a.window_left = window_left < 0 ? -1 : window_left;
   a.cu_q = cu_q;
   a.cu_k = cu_k;
+  a.seqlens_k = seqlens_k;
+  a.kv_rows = seqlen_k;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = fp32 ? fa::launch_fwd_fp32(a, d, s) : fa::launch_fwd_bf16(a, d, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -77,6 +81,18 @@ int fa_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse
                 int window_left, const int* cu_seqlens_q, const int* cu_seqlens_k, void* stream) {
   return fwd_common(true, q, k, v, o, lse, batch, heads, seqlen_q, seqlen_k, d, scale, causal,
                     window_left, cu_seqlens_q, cu_seqlens_k, stream);
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
+                   void* o, float* lse, int batch, int heads, int seqlen_q, int max_len, int d,
+                   float scale, int causal, int window_left, void* stream) {
+  if (seqlens_k == nullptr) return FA_ERR_INVALID_ARG;
+  if (batch > 0 && heads > 0 && seqlen_q > 0 && max_len <= 0) return FA_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr) {
+    if (batch > 0 && heads > 0 && seqlen_q > 0) return FA_ERR_INVALID_ARG;
+  }
+  return fwd_common(false, q, k_cache, v_cache, o, lse, batch, heads, seqlen_q, max_len, d, scale,
+                    causal, window_left, nullptr, nullptr, stream, seqlens_k);
 }
 
 size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int chunk) {

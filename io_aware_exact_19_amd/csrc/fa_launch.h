@@ -22,6 +22,8 @@ struct FwdArgs {
   const int* cu_q;  // varlen offsets, NULL for dense
   const int* cu_k;
   int seg_rows;     // key rows one 32-bit-offset buffer window covers (multiple of 64)
+  const int* seqlens_k;  // KV-cache mode: keys of sequence b are rows [0, seqlens_k[b]) of
+  int kv_rows;           // its kv_rows-row cache block; NULL otherwise
 };
 
 struct DecodeArgs {

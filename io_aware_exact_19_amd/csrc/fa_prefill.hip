@@ -96,13 +96,15 @@ __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
   int bh, t;  // t: rank of the tile in start order, 0 = started first
   if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
     // Tiles differ in length.  Workgroup i goes to XCD i % 8, which starts
-    // its workgroups in order as CUs free up: give XCD x the heads
-    // [x*hx, (x+1)*hx) and let it start all their tiles longest first, so
-    // the short tiles fill in behind the long ones (longest-processing-time
-    // order); each head's tiles stay on one XCD and share its L2.
+    // its workgroups in order as CUs free up: give XCD x the (batch, head)
+    // units x, x + 8, x + 16, ... (a share of every sequence, which matters
+    // when sequences differ in length) and let it start all their tiles
+    // longest first, so the short tiles fill in behind the long ones
+    // (longest-processing-time order); each unit's tiles stay on one XCD and
+    // share its L2.
     const int x = blockIdx.x & 7, k = blockIdx.x >> 3, hx = nbh >> 3;
     t = k / hx;
-    bh = x * hx + (k - t * hx);
+    bh = x + 8 * (k - t * hx);
   } else {
     const int id = xcd_contiguous(blockIdx.x, gridDim.x);
     bh = id / nqt;
@@ -114,10 +116,18 @@ __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
   // bound: earlier tiles see more keys
   w.qt = a.causal || a.window_left < 0 ? nqt - 1 - t : t;
   w.n_q = a.seqlen_q;
-  w.n_k = a.seqlen_k;
   w.q_row0 = (long long)b * a.seqlen_q;
-  w.k_row0 = (long long)b * a.seqlen_k;
   w.lse_base = ((long long)b * a.heads + w.h) * a.seqlen_q;
+  if (a.seqlens_k != nullptr) {
+    // KV cache: the sequence's keys are the first seqlens_k[b] rows of its
+    // kv_rows-row block (clamped to the block); the queries are its last
+    // seqlen_q positions (bottom-right alignment)
+    w.n_k = min(max(a.seqlens_k[b], 0), a.kv_rows);
+    w.k_row0 = (long long)b * a.kv_rows;
+  } else {
+    w.n_k = a.seqlen_k;
+    w.k_row0 = (long long)b * a.seqlen_k;
+  }
 }
 
 // Variable-length scheduler: every wave scans the per-sequence tile counts

@@ -9,6 +9,7 @@ from .attention import (  # noqa: F401
     attention_decode,
     attention_dense,
     attention_flops,
+    attention_kvcache,
     attention_varlen,
     merge_states,
     online_attention,

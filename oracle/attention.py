@@ -49,6 +49,7 @@ __all__ = [
     "attention_dense",
     "attention_varlen",
     "attention_decode",
+    "attention_kvcache",
     "online_attention",
     "merge_states",
     "attention_flops",
@@ -174,6 +175,30 @@ def attention_decode(q, k_cache, v_cache, seqlens_k, scale, heads=None, batches=
             ob, lb = sdpa(q[b, :, h, :], k_cache[b, :n, h, :], v_cache[b, :n, h, :], scale)
             o[b, :, h, :] = ob
             lse[b, h] = lb[0]
+    return o, lse
+
+
+def attention_kvcache(q, k_cache, v_cache, seqlens_k, scale, causal=True, window_left=-1,
+                      heads=None, batches=None):
+    """Several new queries per sequence against its cached keys and values.
+
+    q: [B, n_new, H, d] are the last n_new positions of each sequence;
+    k_cache/v_cache: [B, max_len, H, d]; sequence b's keys are its first
+    seqlens_k[b] rows (the new tokens among them, last).  Masks are relative
+    to the bottom-right diagonal (delta = seqlens_k[b] - n_new), as in
+    ``allowed_mask``.  Rows past the length are never read.  Returns
+    o [B, n_new, H, d] and lse [B, H, n_new]; ``heads``/``batches`` restrict
+    the work to a subset (the rest stays zero).
+    """
+    B, n_new, H, _ = q.shape
+    o = np.zeros((B, n_new, H, v_cache.shape[3]), dtype=np.float64)
+    lse = np.zeros((B, H, n_new), dtype=np.float64)
+    for b in range(B) if batches is None else batches:
+        n = int(seqlens_k[b])
+        for h in range(H) if heads is None else heads:
+            o[b, :, h, :], lse[b, h, :] = sdpa(
+                q[b, :, h, :], k_cache[b, :n, h, :], v_cache[b, :n, h, :], scale, causal,
+                window_left)
     return o, lse
 
 

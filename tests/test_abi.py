@@ -131,6 +131,31 @@ def test_decode_rejects(lib, bad, code):
     assert _dec(**bad) == code
 
 
+def _kvc(**kw):
+    args = dict(q=P, k_cache=P, v_cache=P, seqlens_k=P, o=P, lse=P, batch=4, heads=8,
+                seqlen_q=32, max_len=1000, d=128, scale=0.1, causal=1, window_left=-1,
+                stream=NULL_STREAM)
+    args.update(kw)
+    return fa.fa_fwd_kvcache(**args)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(seqlens_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlens_k=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k_cache=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v_cache=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(max_len=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(batch=0), fa.FA_OK),
+    (dict(seqlen_q=0), fa.FA_OK),
+])
+def test_kvcache_rejects(lib, bad, code):
+    assert _kvc(**bad) == code
+
+
 def test_decode_workspace_size(lib):
     # fp32 chunk outputs [B, H, C, d], 256-byte aligned, then fp32 chunk lse [B, H, C]
     B, H, L, d, c = 64, 32, 32768, 128, 256

@@ -332,6 +332,70 @@ def test_decode_equals_prefill_last_row():
     assert (ld - lp[:, :, 0]).abs().max().item() <= 1e-3
 
 
+def _kvcache_case(B, H, max_len, d, lens, n_new, causal, W, seed, pairs=None):
+    lens = torch.as_tensor(lens, dtype=torch.int32)
+    what = f"kvcache B{B} H{H} max_len{max_len} d{d} new{n_new} causal{int(causal)} W{W}"
+    announce(what)
+    kc = inputs.decode_cache(B, max_len, H, d, lens, seed, "cuda", "k")
+    vc = inputs.decode_cache(B, max_len, H, d, lens, seed, "cuda", "v")
+    q = inputs.normal((B, n_new, H, d), inputs.subseed(seed, "q")).cuda()
+    s = configs.default_scale(d)
+    o, lse = fa.attention_kvcache(q, kc, vc, lens.cuda(), scale=s, causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    o_ref = np.zeros((len(pairs), n_new, d))
+    lse_ref = np.zeros((len(pairs), n_new))
+    got_o = torch.zeros((len(pairs), n_new, d), dtype=torch.bfloat16)
+    got_l = torch.zeros((len(pairs), n_new))
+    qn = _np(q.cpu())
+    for i, (b, h) in enumerate(pairs):
+        n = int(lens[b])
+        o_ref[i], lse_ref[i] = oracle.sdpa(qn[b, :, h], _np(kc[b, :n, h].cpu()),
+                                           _np(vc[b, :n, h].cpu()), s, causal, W)
+        got_o[i], got_l[i] = o[b, :, h], lse[b, h]
+    check(got_o, got_l, o_ref, lse_ref, torch.bfloat16, what)
+    del kc, vc
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_new,causal,W", [(1, True, -1), (5, True, -1), (300, True, -1),
+                                            (300, True, 100), (77, False, -1)])
+def test_kvcache_small(d, n_new, causal, W):
+    """New tokens at the end of cached sequences (NaN past each length), bottom-right causal."""
+    _kvcache_case(3, 4, 1100, d, [1100, 700, 300], n_new, causal, W, seed=47)
+
+
+def test_kvcache_queries_without_keys():
+    """A sequence shorter than the chunk: its first queries see no key (O = 0, lse = -inf)."""
+    _kvcache_case(2, 2, 64, 128, [3, 64], 5, True, -1, seed=48)
+
+
+def test_kvcache_full_cache_equals_dense():
+    """Every length equal to max_len: the cache form is plain dense attention."""
+    B, H, d, L, n = 2, 4, 128, 640, 256
+    q, k, v = (x.cuda() for x in inputs.dense_qkv(B, L, L, H, d, 49))
+    announce("kvcache vs dense")
+    ok, lk = fa.attention_kvcache(q[:, L - n:].contiguous(), k, v,
+                                  torch.full((B,), L, dtype=torch.int32, device="cuda"))
+    od, ld = fa.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ok, od[:, L - n:]) and torch.equal(lk, ld[:, :, L - n:])
+
+
+def test_workload_kvcache():
+    """B8 H32 d128, 512 new tokens against caches of U[1024, 16384] keys (NaN
+    padded): 4 sequences x 2 heads checked against the oracle on all rows."""
+    c = configs.KVCACHE
+    lens = inputs.lengths(c["batch"], c["len_lo"], c["len_hi"], c["seed"]).to(torch.int32)
+    bs = [int(lens.argmax()), int(lens.argmin()), 3, 6]
+    pairs = [(b, h) for b in bs for h in (0, 31)]
+    _kvcache_case(c["batch"], c["heads"], c["max_len"], c["d"], lens, c["n_new"], c["causal"],
+                  -1, c["seed"], pairs)
+    torch.cuda.empty_cache()
+
+
 def test_workload_decode():
     """B64 H32, lengths U[1024, 32768], d128, 256-key chunks, full-size NaN
     padded caches; 8 sequences x 4 heads checked against the oracle."""

@@ -105,6 +105,38 @@ def test_decode_equals_last_row_of_prefill():
         np.testing.assert_allclose(lse[b], lp[0, :, -1], rtol=0, atol=1e-14)
 
 
+def test_kvcache_equals_last_rows_of_prefill():
+    """n_new queries against a cache of L keys (the new tokens last) equal the
+    last n_new rows of causal prefill of length L; with every length equal to
+    max_len the cache form is dense attention; with n_new = 1 it is decode.
+    NaN padding past each length stays out."""
+    r = np.random.default_rng(6)
+    B, H, d, max_len, n_new = 3, 2, 8, 30, 5
+    lens = [30, 12, 5]
+    kc, vc = r.normal(size=(B, max_len, H, d)), r.normal(size=(B, max_len, H, d))
+    for b, n in enumerate(lens):
+        kc[b, n:] = np.nan
+        vc[b, n:] = np.nan
+    q = r.normal(size=(B, n_new, H, d))
+    o, lse = oracle.attention_kvcache(q, kc, vc, lens, 0.3, True, 6)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b, n in enumerate(lens):
+        qq = r.normal(size=(1, n, H, d))
+        qq[0, n - n_new:] = q[b]
+        op, lp = oracle.attention_dense(qq, kc[None, b, :n], vc[None, b, :n], 0.3, True, 6)
+        np.testing.assert_allclose(o[b], op[0, n - n_new:], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[b], lp[0, :, n - n_new:], rtol=0, atol=1e-14)
+    kf, vf = r.normal(size=(B, max_len, H, d)), r.normal(size=(B, max_len, H, d))
+    o1, l1 = oracle.attention_kvcache(q, kf, vf, [max_len] * B, 0.3, False)
+    o2, l2 = oracle.attention_dense(q, kf, vf, 0.3, False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    o3, l3 = oracle.attention_kvcache(q[:, -1:], kc, vc, lens, 0.3, True)
+    o4, l4 = oracle.attention_decode(q[:, -1:], kc, vc, lens, 0.3)
+    np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l3[:, :, 0], l4, rtol=0, atol=1e-14)
+
+
 @pytest.mark.parametrize("chunk", [1, 4, 7, 256])
 def test_merge_of_chunks_equals_unsplit(chunk):
     """Attention over disjoint key chunks, merged by lse weights, equals
