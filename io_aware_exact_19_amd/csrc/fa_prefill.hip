@@ -144,6 +144,10 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
     const int inc = wave_inclusive_scan(nt, lane);
     total += __shfl(inc, 63, 64);
   }
+  // every lane holds the same values; say so, so that the work decode stays
+  // in scalar registers (else the tile loop and the buffer descriptors built
+  // from it would be treated as divergent)
+  total = __builtin_amdgcn_readfirstlane(total);
   const long long live = (long long)total * a.heads;
   if ((long long)blockIdx.x >= live) return false;
   const int id = xcd_contiguous(blockIdx.x, (int)live);
@@ -159,8 +163,8 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
     if (hit) {
       const int src = __builtin_ctzll(hit);
       const int seq = s0 + src;
-      const int t = g - __shfl(exc, src, 64);
-      const int ntq = __shfl(nt, src, 64);
+      const int t = g - __builtin_amdgcn_readfirstlane(__shfl(exc, src, 64));
+      const int ntq = __builtin_amdgcn_readfirstlane(__shfl(nt, src, 64));
       const int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
       const int ck0 = a.cu_k[seq], ck1 = a.cu_k[seq + 1];
       w.qt = ntq - 1 - t;
@@ -171,7 +175,7 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
       w.lse_base = (long long)w.h * a.cu_q[nseq] + cq0;
       return true;
     }
-    base = __shfl(inc, 63, 64);
+    base = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
   }
   return false;
 }
@@ -704,10 +708,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
   fwd_bf16_body<D, VARLEN>(a);
 }
 
-// The four-wave kernel moves its running max only when a row's new max
-// exceeds it by more than this (base-2 units): the output u / l does not
-// depend on which reference max is used, and probabilities stay <= 2^8.
-constexpr float kRescaleSlack4 = 8.0f;
+// The four-wave kernel keeps its reference max while a lane's probabilities
+// against it sum to at most this bound: the output u / l does not depend on
+// which reference max is used, and probabilities stay <= 2^8.
+constexpr float kLazyBound4 = 256.0f;
 
 // Queue the DMA of K/V tile rows [k0, k0 + kBC) of one head straight into
 // LDS (no registers).  The buffer descriptor covers only the rows that exist,
@@ -745,7 +749,8 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char k_lds1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds1[T::kBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps row ranges scalar
   const int half = lane >> 5, l32 = lane & 31;
   const int grp = lane >> 4, j16 = lane & 15;
 
@@ -850,46 +855,57 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
     const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
                            (W >= 0 && k0 < wq_last + delta - W);
     if (need_mask) {
+      // allowed keys of this lane's row: [lo, hi]; key kj = k0 + 8 half + c
+      // is allowed iff (kj - lo) and (hi - kj) are both >= 0: their sign bits
+      // make a select mask (no compare results in scalar registers)
+      int hi = n_k - 1, lo = 0;
+      if (causal) hi = min(hi, qi + delta);
+      if (W >= 0) lo = max(lo, qi + delta - W);
+      const int e = k0 + 8 * half - lo, f = hi - k0 - 8 * half;
 #pragma unroll
       for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kj = k0 + kb * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-          const bool ok = kj < n_k && (!causal || kj <= qi + delta) &&
-                          (W < 0 || kj >= qi + delta - W);
-          if (!ok) sacc[kb][r] = kNegInf;
+          const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
+          const uint32_t bad = (uint32_t)(((e + c) | (f - c)) >> 31);
+          sacc[kb][r] = __uint_as_float((bad & 0xff800000u) | (~bad & __float_as_uint(sacc[kb][r])));
         }
     }
 
-    // online softmax update, base 2, lazy reference max
-    float mx = kNegInf;
+    // online softmax update, base 2, lazy reference max: probabilities
+    // against the current reference are accepted when this lane's 32 of them
+    // sum to at most kLazyBound4 (so none exceeds it); otherwise (a
+    // row's first live tile, whose reference is -inf, or a jump of the row
+    // max) the reference moves to the tile max, the state is rescaled and
+    // the probabilities recomputed
+    float p[kBC / 32][16];
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    const float m_tile = max_halves(mx) * c2;
-    const bool grow = m_tile > m_run + kRescaleSlack4;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha = grow ? exp2_hw(m_run - m_new) : 1.0f;
+      for (int r = 0; r < 16; ++r) p[kb][r] = exp2_hw(fmaf(sacc[kb][r], c2, -m_run));
+    float rsum = tree_sum<kBC / 32>(p);
+    if (__builtin_amdgcn_ballot_w64(!(rsum <= kLazyBound4)) != 0) {
+      const float m_tile = max_halves(tree_max<kBC / 32>(sacc)) * c2;
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_new == m_run ? 1.0f : exp2_hw(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
+      const float m_use = m_run == kNegInf ? 0.0f : m_run;
+#pragma unroll
+      for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[kb][r] = exp2_hw(fmaf(sacc[kb][r], c2, -m_use));
+      rsum = tree_sum<kBC / 32>(p);
     }
-    const float m_use = m_run == kNegInf ? 0.0f : m_run;
-    float rsum = 0.0f;
+    l_run += rsum;
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(fmaf(sacc[kb][r], c2, -m_use));
-        sacc[kb][r] = p;
-        rsum += p;
-      }
-    l_run += rsum;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = p[kb][r];
 
 #pragma unroll
     for (int ks = 0; ks < kBC / 16; ++ks) {
