@@ -16,8 +16,9 @@ timed steps.  The line also carries:
   same workload;
 * ``secondary``: the other workloads (causal 2k, 8000-token causal prompt,
   packed varlen with a 1024-key window, fp32 small case, KV-cache decode in
-  HBM GB/s, and chunked prefill of 512 new tokens against KV caches), each
-  timed the same way.
+  HBM GB/s, chunked prefill of 512 new tokens against KV caches, and the
+  backward pass of the headline shape, plain and causal), each timed the same
+  way.
 
 Every workload first runs back to back for ``--settle-ms`` (default 400 ms)
 so that the engine clock has left its idle ramp before the warmup steps.
@@ -190,6 +191,35 @@ def make_kvcache(torch, fa, inputs, configs, cfg):
     w = Workload(cfg["name"], launch, 4 * d * H * pairs, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma",
                  "bf16", conf)
     w.tensors = (kc, vc)
+    return w
+
+
+def make_backward(torch, fa, inputs, configs, cfg, causal=False):
+    """dQ, dK, dV of the headline shape from o and lse of one forward call."""
+    B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
+    q, k, v = (x.cuda() for x in inputs.dense_qkv(B, N, N, H, d, cfg["seed"]))
+    do = inputs.normal((B, N, H, d), inputs.subseed(cfg["seed"], "dout")).cuda()
+    s = configs.default_scale(d)
+    o, lse = fa.attention(q, k, v, scale=s, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa.fa_bwd_workspace_size(B, H, N)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, N, d, s, int(causal), -1, ws, need,
+                       stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_bwd")
+
+    pairs = N * (N + 1) // 2 if causal else N * N
+    name = f"backward_bf16_b{B}_h{H}_n{N}_d{d}" + ("_causal" if causal else "")
+    # the usual count: 2.5x the forward (score recompute, dV, dP, dQ, dK products)
+    conf = dict(workload=name, batch=B, heads=H, seqlen=N, d=d, causal=causal,
+                flops="2.5 x forward (5 products of 2 N^2 d per head)")
+    w = Workload(name, launch, 10 * d * H * B * pairs, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma", "bf16",
+                 conf)
+    w.tensors = (q, k, v, do, o, lse)
     return w
 
 
@@ -375,7 +405,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-target", default=None,
                     choices=["prefill_2k", "prefill_2k_causal", "long_8k", "varlen", "small_fp32",
-                             "decode", "kvcache"])
+                             "decode", "kvcache", "backward", "backward_causal"])
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-target", default="prefill_2k")
@@ -418,6 +448,9 @@ def main():
                                          dtype_name="f32"),
         "decode": lambda: make_decode(torch, fa, inputs, configs, configs.DECODE),
         "kvcache": lambda: make_kvcache(torch, fa, inputs, configs, configs.KVCACHE),
+        "backward": lambda: make_backward(torch, fa, inputs, configs, configs.PREFILL_2K),
+        "backward_causal": lambda: make_backward(torch, fa, inputs, configs, configs.PREFILL_2K,
+                                                 causal=True),
     }
 
     if args.profile_target:
@@ -475,7 +508,8 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode", "kvcache"):
+        for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode", "kvcache",
+                    "backward", "backward_causal"):
             w = builders[key]()
             steps = 20 if key != "decode" else 10
             log(f"[bench] timing {w.name}")

@@ -117,6 +117,33 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
                    int window_left, void* stream);
 
 /*
+ * fa_bwd_workspace_size -- bytes of device workspace fa_bwd needs: two fp32
+ * values per (batch, head, query row).  Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q);
+
+/*
+ * fa_bwd -- attention backward (dense), bf16: the gradients dQ, dK, dV of
+ * O = softmax(scale Q K^T) V for an output gradient dO, with the masks of
+ * fa_fwd.  The probabilities are recomputed from the row log-sum-exp lse that
+ * fa_fwd emitted (the use the pages give for keeping it: "FlashAttention"
+ * (aiwiki.page), section "Training and computational complexity").
+ *   q, o, dout, dq: [batch, seqlen_q, heads, d] bf16 (o and lse from fa_fwd
+ *                   on the same q, k, v, scale and masks);
+ *   k, v, dk, dv:   [batch, seqlen_k, heads, d] bf16;
+ *   lse:            [batch, heads, seqlen_q] fp32 (natural log; -inf for rows
+ *                   with no allowed key, whose dq is 0).
+ * d: 64 or 128.  Keys that no query sees get dk = dv = 0.  workspace_bytes
+ * must be at least fa_bwd_workspace_size(batch, heads, seqlen_q).  Every
+ * output element is written once (no atomics), so results are deterministic.
+ * FA_ERR_UNSUPPORTED when 128 rows of one tensor span 2 GiB or more.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int seqlen_q,
+           int seqlen_k, int d, float scale, int causal, int window_left, void* workspace,
+           size_t workspace_bytes, void* stream);
+
+/*
  * fa_decode_workspace_size -- bytes of device workspace fa_decode needs:
  * per (batch, head, chunk) an fp32 partial output of d values and one fp32
  * partial log-sum-exp, chunks = ceil(max_len / chunk).  Returns 0 for

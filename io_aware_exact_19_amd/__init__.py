@@ -13,9 +13,12 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     FAError,
     attention,
+    attention_backward,
     attention_kvcache,
     attention_varlen,
     decode,
+    fa_bwd,
+    fa_bwd_workspace_size,
     fa_decode,
     fa_decode_workspace_size,
     fa_fwd,

@@ -29,8 +29,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_decode_workspace_size", "fa_decode",
-            "fa_status_string")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_decode_workspace_size", "fa_decode", "fa_status_string")
 
 _lib = None
 
@@ -59,6 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_fp32.restype = I
     lib.fa_fwd_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_fwd_kvcache.restype = I
+    lib.fa_bwd_workspace_size.argtypes = [I, I, I]
+    lib.fa_bwd_workspace_size.restype = Z
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P]
+    lib.fa_bwd.restype = I
     lib.fa_decode_workspace_size.argtypes = [I, I, I, I, I]
     lib.fa_decode_workspace_size.restype = Z
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
@@ -108,6 +112,18 @@ def fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, seqlen_
     return load_library().fa_fwd_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k),
                                          _ptr(o), _ptr(lse), batch, heads, seqlen_q, max_len, d,
                                          scale, int(causal), window_left, _stream(stream))
+
+
+def fa_bwd_workspace_size(batch, heads, seqlen_q) -> int:
+    return int(load_library().fa_bwd_workspace_size(batch, heads, seqlen_q))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads, seqlen_q, seqlen_k, d, scale, causal,
+           window_left, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), batch, heads, seqlen_q, seqlen_k,
+                                 d, scale, int(causal), window_left, _ptr(workspace),
+                                 workspace_bytes, _stream(stream))
 
 
 def fa_decode_workspace_size(batch, heads, max_len, d, chunk) -> int:
@@ -217,6 +233,32 @@ def attention_kvcache(q, k_cache, v_cache, seqlens_k, *, scale=None, causal=True
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache")
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, window_left=-1,
+                       workspace=None, stream=None):
+    """Gradients of dense bf16 attention: q/o/dout [B, n_q, H, d], k/v
+    [B, n_k, H, d], lse [B, H, n_q] fp32 from ``attention``.  Returns
+    (dq, dk, dv)."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, torch.bfloat16, 4)
+    _check_tensor("lse", lse, torch.float32, 3)
+    B, n_q, H, d = q.shape
+    n_k = k.shape[1]
+    if k.shape != (B, n_k, H, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, H, n_q):
+        raise ValueError("lse must be [B, H, n_q]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa_bwd_workspace_size(B, H, n_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, n_q, n_k, d, s, int(causal),
+                int(window_left), workspace, workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seqlens_k, *, scale=None, chunk=256, workspace=None,

@@ -95,6 +95,63 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, cons
                     causal, window_left, nullptr, nullptr, stream, seqlens_k);
 }
 
+size_t fa_bwd_workspace_size(int batch, int heads, int seqlen_q) {
+  if (batch <= 0 || heads <= 0 || seqlen_q <= 0) return 0;
+  return 2 * (size_t)batch * heads * seqlen_q * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int seqlen_q,
+           int seqlen_k, int d, float scale, int causal, int window_left, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (batch == 0 || heads == 0 || (seqlen_q == 0 && seqlen_k == 0)) return FA_OK;
+  const bool rows = seqlen_q > 0, keys = seqlen_k > 0;
+  if (rows && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
+    return FA_ERR_INVALID_ARG;
+  if (keys && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_size(batch, heads, seqlen_q);
+  if (rows && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return FA_ERR_WORKSPACE;
+  // each workgroup addresses 128 rows of one head with 32-bit offsets
+  const unsigned long long row_bytes = (unsigned long long)heads * d * 2;
+  if (row_bytes * 128 >= 0x80000000ull) return FA_ERR_UNSUPPORTED;
+  const long long g = (long long)batch * heads * ((seqlen_q > seqlen_k ? seqlen_q : seqlen_k) + 127) / 128;
+  if (g > 0x7fffffffLL || (long long)batch * heads * seqlen_q > 0x7fffffffLL * 256LL)
+    return FA_ERR_UNSUPPORTED;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws_d = static_cast<float*>(workspace);
+  a.ws_l2 = rows ? static_cast<float*>(workspace) + (size_t)batch * heads * seqlen_q : nullptr;
+  a.batch = batch;
+  a.heads = heads;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  const hipError_t e = fa::launch_bwd(a, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int chunk) {
   if (batch <= 0 || heads <= 0 || max_len <= 0 || d <= 0 || chunk <= 0) return 0;
   const int max_chunks = (max_len + chunk - 1) / chunk;

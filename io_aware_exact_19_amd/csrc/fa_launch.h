@@ -53,4 +53,28 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;       // [batch, seqlen_q, heads, d] bf16
+  const void* k;       // [batch, seqlen_k, heads, d] bf16
+  const void* v;
+  const void* o;       // forward output, layout of q
+  const void* dout;    // gradient of the loss with respect to o
+  const float* lse;    // [batch, heads, seqlen_q] natural-log row log-sum-exp
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws_d;         // [batch, heads, seqlen_q] rowsum(dO o O)
+  float* ws_l2;        // [batch, heads, seqlen_q] lse * log2(e)
+  int batch;
+  int heads;
+  int seqlen_q;
+  int seqlen_k;
+  float scale;
+  float scale_log2;
+  int causal;
+  int window_left;
+};
+
+hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream);
+
 }  // namespace fa

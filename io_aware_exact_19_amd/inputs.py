@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import torch
 
-_STREAM = {"q": 1, "k": 2, "v": 3, "lengths": 4}
+_STREAM = {"q": 1, "k": 2, "v": 3, "lengths": 4, "dout": 5}
 
 
 def subseed(seed: int, name: str, index: int = 0) -> int:

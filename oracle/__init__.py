@@ -7,6 +7,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 from .attention import (  # noqa: F401
     allowed_mask,
     attention_decode,
+    attention_backward,
     attention_dense,
     attention_flops,
     attention_kvcache,
@@ -14,4 +15,5 @@ from .attention import (  # noqa: F401
     merge_states,
     online_attention,
     sdpa,
+    sdpa_backward,
 )

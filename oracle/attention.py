@@ -23,6 +23,15 @@ What it computes, and where the pages fix it:
   output u / l -- "FlashAttention", section "Tiling and online
   normalisation", the three update equations and the final division.  It is
   used by the tests to pin the recurrence against the 3-pass definition.
+* ``sdpa_backward`` / ``attention_backward`` are the gradients of the same
+  definition with respect to Q, K and V for an output gradient dO, by the
+  chain rule through the materialised softmax: dV = P^T dO, dP = dO V^T,
+  dS = P o (dP - rowsum(dO o O)), dQ = scale dS K, dK = scale dS^T Q.  The
+  pages keep the row log-sum-exp exactly so that the backward pass can
+  recompute P instead of storing it ("FlashAttention", section "Training and
+  computational complexity"); the gradient formulas themselves are the
+  textbook derivative of softmax(S) V, pinned in the tests by central finite
+  differences.
 * ``merge_states`` combines per-chunk (o_c, lse_c) pairs.  The pages do not
   name split-KV; the merge is the same rescale-and-add as the recurrence above
   applied to whole chunk states (a chunk state (m_c, l_c, u_c) has
@@ -50,6 +59,8 @@ __all__ = [
     "attention_varlen",
     "attention_decode",
     "attention_kvcache",
+    "sdpa_backward",
+    "attention_backward",
     "online_attention",
     "merge_states",
     "attention_flops",
@@ -111,6 +122,55 @@ def sdpa(q, k, v, scale, causal=False, window_left=-1, q_index=None, n_q=None):
     o[live] = p @ v
     lse[live] = m + np.log(l)
     return o, lse
+
+
+def sdpa_backward(q, k, v, do, scale, causal=False, window_left=-1):
+    """Gradients of one head of attention, materialised, fp64.
+
+    q: [n_q, d], k: [n_k, d], v: [n_k, d_v], do: [n_q, d_v] (the gradient of
+    the loss with respect to O).  P is the row softmax of the masked scores
+    (3-pass, rows with no allowed key have P = 0).  Returns dq [n_q, d],
+    dk [n_k, d], dv [n_k, d_v].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n_q, n_k = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    ok = allowed_mask(n_q, n_k, causal, window_left)
+    s = np.where(ok, s, -np.inf)
+    p = np.zeros_like(s)
+    live = ok.any(axis=1)
+    if live.any():
+        sl = s[live]
+        m = sl.max(axis=1)
+        e = np.exp(sl - m[:, None])
+        p[live] = e / e.sum(axis=1)[:, None]
+    o = p @ v
+    dv = p.T @ do                          # O = P V
+    dp = do @ v.T
+    dsum = (do * o).sum(axis=1)            # = rowsum(P o dP)
+    ds = p * (dp - dsum[:, None])          # softmax Jacobian applied to dP, row by row
+    dq = scale * (ds @ k)                  # S = scale Q K^T
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale, causal=False, window_left=-1):
+    """Dense batched gradients: q/do [B, n_q, H, d], k/v [B, n_k, H, d];
+    returns dq, dk, dv in the same layouts, fp64, one ``sdpa_backward`` per
+    (batch, head)."""
+    q = np.asarray(q)
+    B, n_q, H, d = q.shape
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            dq[b, :, h], dk[b, :, h], dv[b, :, h] = sdpa_backward(
+                q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], scale, causal, window_left)
+    return dq, dk, dv
 
 
 def attention_dense(q, k, v, scale, causal=False, window_left=-1):

@@ -156,6 +156,37 @@ def test_kvcache_rejects(lib, bad, code):
     assert _kvc(**bad) == code
 
 
+def _bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, batch=2, heads=4, seqlen_q=64,
+                seqlen_k=64, d=128, scale=0.1, causal=0, window_left=-1, workspace=P,
+                workspace_bytes=1 << 20, stream=NULL_STREAM)
+    args.update(kw)
+    return fa.fa_bwd(**args)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=P + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(workspace=0), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=2 * 2 * 4 * 64 * 4 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(batch=0), fa.FA_OK),
+])
+def test_bwd_rejects(lib, bad, code):
+    assert _bwd(**bad) == code
+
+
+def test_bwd_workspace_size(lib):
+    assert fa.fa_bwd_workspace_size(2, 4, 64) == 2 * 2 * 4 * 64 * 4
+    assert fa.fa_bwd_workspace_size(0, 4, 64) == 0
+
+
 def test_decode_workspace_size(lib):
     # fp32 chunk outputs [B, H, C, d], 256-byte aligned, then fp32 chunk lse [B, H, C]
     B, H, L, d, c = 64, 32, 32768, 128, 256

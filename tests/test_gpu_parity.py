@@ -9,6 +9,7 @@ batch) and on sampled (sequence, head) pairs (decode).
 """
 
 import math
+import sys
 
 import numpy as np
 import pytest
@@ -330,6 +331,49 @@ def test_decode_equals_prefill_last_row():
     torch.cuda.synchronize()
     assert (od.float() - op.float()).abs().max().item() <= 2e-2
     assert (ld - lp[:, :, 0]).abs().max().item() <= 1e-3
+
+
+# Backward tolerance, relative to the largest reference gradient entry of each
+# tensor: P and dS are rounded to bf16 before their products (relative error
+# up to 2^-8 each), D = rowsum(dO o O) uses the bf16 forward output, and the
+# gradients are rounded to bf16 once; each stays well inside 2 % of the
+# tensor's largest entry at the element level and 0.2 % on average.
+BWD_MAX_REL = 2e-2
+BWD_MEAN_REL = 2e-3
+
+
+def _bwd_case(B, H, n_q, n_k, d, causal, W, seed, q_mult=1.0):
+    what = f"bwd B{B} H{H} nq{n_q} nk{n_k} d{d} causal{int(causal)} W{W} x{q_mult}"
+    announce(what)
+    q, k, v = inputs.dense_qkv(B, n_q, n_k, H, d, seed, torch.bfloat16, q_mult)
+    do = inputs.normal((B, n_q, H, d), inputs.subseed(seed, "dout"))
+    s = configs.default_scale(d)
+    qc, kc, vc, dc = (x.cuda() for x in (q, k, v, do))
+    o, lse = fa.attention(qc, kc, vc, scale=s, causal=causal, window_left=W)
+    dq, dk, dv = fa.attention_backward(qc, kc, vc, o, lse, dc, scale=s, causal=causal,
+                                       window_left=W)
+    torch.cuda.synchronize()
+    refs = oracle.attention_backward(_np(q), _np(k), _np(v), _np(do), s, causal, W)
+    msg = []
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        g = _np(got.cpu())
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        top = max(float(np.abs(ref).max()), 1e-30)
+        err = np.abs(g - ref) / top
+        msg.append(f"{name} max {err.max():.2e} mean {err.mean():.2e} (of {top:.2e})")
+        assert err.max() <= BWD_MAX_REL, f"{what}: {name} max rel {err.max():.3e}"
+        assert err.mean() <= BWD_MEAN_REL, f"{what}: {name} mean rel {err.mean():.3e}"
+    print(f"[parity] {what}: " + "; ".join(msg), file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_q,n_k,causal,W,qm", [(300, 300, False, -1, 1.0), (257, 700, True, -1, 1.0),
+                                                 (1000, 1000, True, 100, 1.0), (129, 64, False, -1, 1.0),
+                                                 (512, 512, True, -1, 4.0)])
+def test_backward(d, n_q, n_k, causal, W, qm):
+    """dQ, dK, dV against the fp64 oracle's chain rule on the same bf16 inputs,
+    with o and lse from the forward kernel."""
+    _bwd_case(2, 3, n_q, n_k, d, causal, W, seed=71, q_mult=qm)
 
 
 def _kvcache_case(B, H, max_len, d, lens, n_new, causal, W, seed, pairs=None):

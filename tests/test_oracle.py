@@ -137,6 +137,67 @@ def test_kvcache_equals_last_rows_of_prefill():
     np.testing.assert_allclose(l3[:, :, 0], l4, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("causal,window", [(False, -1), (True, -1), (True, 2), (False, 1)])
+def test_backward_matches_finite_differences(causal, window):
+    """dQ, dK, dV of L = sum(O o dO) against central differences of the
+    forward definition (n_q != n_k, so bottom-right masks and, with the
+    window, rows and keys that see nothing are exercised)."""
+    r = np.random.default_rng(11)
+    n_q, n_k, d, dv_ = 5, 7, 3, 4
+    q, k = r.normal(size=(n_q, d)), r.normal(size=(n_k, d))
+    v, do = r.normal(size=(n_k, dv_)), r.normal(size=(n_q, dv_))
+    scale = 0.7
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, do, scale, causal, window)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.sdpa(qq, kk, vv, scale, causal, window)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for x, g, idx in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[idx], args_m[idx] = xp, xm
+            num[pos] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_invariants():
+    """Row sums of dS vanish, so the key gradients sum to zero over the keys;
+    shifting every key by one vector shifts each score row by a constant,
+    which changes neither P nor O: dQ and dV stay the same."""
+    r = np.random.default_rng(12)
+    n, d = 9, 4
+    q, k, v, do = (r.normal(size=(n, d)) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv = oracle.sdpa_backward(q, k, v, do, 0.5, causal)
+        np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+        w = r.normal(size=d)
+        dq2, _, dv2 = oracle.sdpa_backward(q, k + w[None, :], v, do, 0.5, causal)
+        np.testing.assert_allclose(dq2, dq, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv2, dv, rtol=0, atol=1e-12)
+
+
+def test_backward_matches_autograd():
+    """Cross-check with PyTorch's autograd (fp64, CPU) through its own SDPA."""
+    torch = pytest.importorskip("torch")
+    r = np.random.default_rng(13)
+    B, n, H, d = 2, 11, 2, 8
+    q, k, v, do = (r.normal(size=(B, n, H, d)) for _ in range(4))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, 0.3, True)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.3)
+    o.backward(torch.tensor(do.transpose(0, 2, 1, 3)))
+    for got, ref in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(got, ref.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10,
+                                   atol=1e-12)
+
+
 @pytest.mark.parametrize("chunk", [1, 4, 7, 256])
 def test_merge_of_chunks_equals_unsplit(chunk):
     """Attention over disjoint key chunks, merged by lse weights, equals
