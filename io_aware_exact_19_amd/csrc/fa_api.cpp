@@ -138,8 +138,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.ws_d = static_cast<float*>(workspace);
-  a.ws_l2 = rows ? static_cast<float*>(workspace) + (size_t)batch * heads * seqlen_q : nullptr;
+  a.ws_nd = static_cast<float*>(workspace);
+  a.ws_nl = rows ? static_cast<float*>(workspace) + (size_t)batch * heads * seqlen_q : nullptr;
   a.batch = batch;
   a.heads = heads;
   a.seqlen_q = seqlen_q;

@@ -8,25 +8,39 @@
 //   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels, no atomics (every output element has one writer):
-//  * prep: D_i and the base-2 lse (lse * log2 e) per row, into the workspace.
-//  * dkdv: one workgroup of 4 waves per (batch, head, 128 keys); each wave
-//    owns 32 keys and keeps their K and V fragments in registers while
-//    64-row tiles of Q and dO stream through LDS.  Per 32 query rows it
-//    forms S = Q K^T and dP = dO V^T (keys in the lane, rows in the
-//    accumulator registers), P and dS on the VALU, then accumulates
+//  * prep: -D_i and -lse_i / scale per row, into the workspace.  They seed
+//    the dP and S accumulators, so the products come out as dP - D and
+//    S - lse / scale and the VALU needs one multiply less per element.
+//  * dkdv: one workgroup of 4 waves (one per SIMD) per (batch, head, 128
+//    keys); each wave owns 32 keys and keeps their K and V fragments in
+//    registers while 64-row tiles of Q, dO, -lse/scale, -D stream through a ring
+//    of LDS slots.  Per 32 query rows: S = Q K^T and dP = dO V^T (keys in the
+//    lane, rows in the accumulator registers), P and dS on the VALU, then
 //    dV^T += dO^T P and dK^T += Q^T dS with the tile read transposed.
 //  * dq: one workgroup per (batch, head, 128 query rows); each wave owns 32
 //    rows (Q and dO fragments in registers) while 64-key tiles of K and V
-//    stream through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T on the VALU, then
-//    dQ^T += K^T dS^T.
+//    stream through the ring: S^T = K Q^T, dP^T = V dO^T, dS^T on the VALU,
+//    then dQ^T += K^T dS^T.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs neither
+// atomics nor an fp32 dQ buffer, and the result is bit-reproducible.
+//
 // All products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS
-// are rounded to bf16 before they enter a product.  The operand layouts are
-// those of the forward kernel: the query (or key) rows that form a score
-// accumulator enter in pi order (bits 2 and 3 of the row index swapped), so
-// each lane's accumulator registers are directly the k-slots of the next
-// product's operand, and transposed operands come from ds_read_b64_tr_b16.
+// are rounded to bf16 before they enter a product.  The rows that form a
+// score accumulator enter in pi order (bits 2 and 3 of the row index
+// swapped), so each lane's accumulator registers are directly the k-slots of
+// the next product's operand, and transposed operands come from
+// ds_read_b64_tr_b16.
+//
+// Each wave runs a three-stage software pipeline over 32-row (32-key) blocks:
+// one step issues the score products of block j+1 and the gradient products
+// of block j-1 on the matrix pipe, interleaved, while the VALU turns the
+// scores of block j into P and dS.  With one wave per SIMD this is what keeps
+// the matrix pipe fed.
 #include "fa_common.h"
 #include "fa_launch.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace fa {
 namespace {
@@ -35,12 +49,27 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __attribute__((address_space(3))) float lds_float_t;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 
-constexpr int kBThreads = 256;  // 4 waves
-constexpr int kWaveRows = 32;   // keys (dkdv) or query rows (dq) owned by one wave
-constexpr int kTile = 64;       // rows of a streamed LDS tile
-constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kBThreads = 256;                 // 4 waves, one per SIMD
+constexpr int kBWaves = 4;
+constexpr int kWaveRows = 32;                  // keys (dkdv) or query rows (dq) of one wave
+constexpr int kUnit = kBWaves * kWaveRows;     // keys or rows of one workgroup
+constexpr int kTile = 64;                      // rows of a streamed tile
+constexpr int kRing = 4;                       // tile slots in LDS
+constexpr int kLook = 4;                       // operand fragments read ahead of their product
+constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
+constexpr int kFar = 1 << 28;                  // an unbounded side of a mask interval
+
+template <int D>
+struct BTile {
+  static constexpr int kCh = D / 8;                       // 16-byte chunks per row
+  static constexpr int kRowB = D * 2;                     // bytes per row in LDS
+  static constexpr int kBytes = kTile * kRowB;            // one tensor's tile
+  static constexpr int kLoads = kBytes / 1024 / kBWaves;  // 1 KB DMA loads per wave per tensor
+  static constexpr int kVec = kTile * 4;                  // one fp32 value per tile row
+  static_assert(kBytes % (1024 * kBWaves) == 0, "tile must split evenly over the waves");
+};
 
 // The 32 rows behind a 32x32 score accumulator enter in this order, so that
 // lane half h, register r holds logical row 16 (r / 8) + 8 h + (r % 8).
@@ -48,69 +77,204 @@ __device__ __forceinline__ int pi_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-// LDS tile of kTile rows x D bf16, rows padded by 16 bytes
+// Tiles are read two ways: by rows (16 lanes take one 16-byte chunk of 16
+// consecutive rows) and transposed (32 lanes take 4 chunks of 4 consecutive
+// rows).  Chunk c of row r sits at c ^ bswz(r): within any 16 aligned rows the
+// swizzles are distinct (row reads hit 16 different bank groups), and within
+// any 4 aligned rows the group of 4 chunks they select differs (transposed
+// reads too).  At d = 64 two rows share a 256-byte bank line, so the row
+// parity already separates neighbours and the swizzle uses r >> 1.
 template <int D>
-constexpr int row_stride() { return D * 2 + 16; }
-
-// buffer descriptor over [p, p + bytes); offsets past the end read zeros
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), 0,
-                                           __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
-}
-
-// rows [row0, row0 + kTile) of a [rows][heads][D] bf16 tensor (head base g,
-// rs elements between rows) into an LDS tile; rows >= n become zeros
-template <int D>
-__device__ __forceinline__ void stage_tile(char* lds, const uint16_t* g, long long rs, int row0,
-                                           int n, int tid) {
-  constexpr int kCh = D / 8;                    // 16-byte chunks per row
-  constexpr int kPer = kTile * kCh / kBThreads;  // chunks per thread
-  const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const int rows = max(min(n - row0, kTile), 0);
-  const __amdgpu_buffer_rsrc_t r = rsrc_of(g + (long long)max(row0, 0) * rs, (uint32_t)rows * row_bytes);
-  u32x4_t x[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * kBThreads + tid, row = c / kCh, ch = c % kCh;
-    x[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)row * row_bytes + ch * 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int c = i * kBThreads + tid, row = c / kCh, ch = c % kCh;
-    *(lds_bf16x8_t*)((lds_void_t*)(lds + row * row_stride<D>() + ch * 16)) =
-        __builtin_bit_cast(bf16x8_t, x[i]);
+__device__ __forceinline__ int bswz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
 }
 
-// Operand fragment with rows as the reduction index, read transposed from an
-// LDS tile: lane l gets tile[row0 + 8 h + 0..7][32 db + l % 32] for the
-// k-slice starting at row0 (h = lane half); row0 is a multiple of 16.
-template <int D>
-__device__ __forceinline__ bf16x8_t tr_frag(const char* lds, int row0, int db, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const int row = row0 + 8 * (g >> 1) + (j >> 2);
-  const int d = db * 32 + 16 * (g & 1) + 4 * (j & 3);
-  const char* p = lds + row * row_stride<D>() + d * 2;
-  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_void_t*)p));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16_t*)((lds_void_t*)(p + 4 * row_stride<D>())));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+__device__ __forceinline__ u32x4_t rsrc_of(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcWord3;
+  return r;
 }
 
-// Operand fragment with d as the reduction index: tile[row][16 kk + 8 h .. + 7]
-template <int D>
-__device__ __forceinline__ bf16x8_t row_frag(const char* lds, int row, int kk, int half) {
-  return *(const lds_bf16x8_t*)((const lds_void_t*)(lds + row * row_stride<D>() + (kk * 16 + half * 8) * 2));
+// 16 (or 4) bytes per lane from the buffer at byte offset voff straight into
+// LDS at lds_base + 16 (or 4) * lane; offsets past the descriptor's size read
+// zeros.  Inline assembly keeps the loads out of the compiler's wait
+// tracking: the only waits for them are the explicit vmcnt waits before the
+// barriers, so LDS reads of other ring slots never wait for them.
+__device__ __forceinline__ void dma_b128(const u32x4_t& rs, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rs), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void dma_b32(const u32x4_t& rs, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rs), "s"(lds_base)
+      : "memory");
 }
 
-// key j allowed for query i (delta = n_k - n_q)
-__device__ __forceinline__ bool allowed(const BwdArgs& a, int i, int j, int delta) {
-  return i < a.seqlen_q && j < a.seqlen_k && (!a.causal || j <= i + delta) &&
-         (a.window_left < 0 || j >= i + delta - a.window_left);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)p);
 }
+
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Workgroup barrier with no implicit wait (see the DMA helpers).
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ bf16x8_t lds_row(const char* p) {
+  return *(const lds_bf16x8_t*)((const lds_void_t*)p);
+}
+__device__ __forceinline__ bf16x8_t lds_tr(const char* lo, const char* hi) {
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_void_t*)lo));
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)((lds_void_t*)hi));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ f32x4_t lds_f4(const char* p) {
+  return *(const lds_f32x4_t*)((const lds_void_t*)p);
+}
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane byte offsets of the two operand reads inside one tile.
+//  row[kk]: the row-wise fragment of 32-row block 0 (rows in pi order) with
+//           d = 16 kk + 8 h .. + 7 (the reduction index of S and dP);
+//  tlo/thi[db]: the transposed fragment of 16-row slice 0, columns
+//           32 db + l % 32, rows 8 h .. + 3 and 8 h + 4 .. + 7.
+// Other blocks and slices add a multiple of 16 rows, which keeps the swizzle.
+template <int D>
+struct FragOffsets {
+  int row[D / 16];
+  int tlo[D / 32];
+  int thi[D / 32];
+  __device__ __forceinline__ explicit FragOffsets(int lane) {
+    using T = BTile<D>;
+    const int half = lane >> 5, rr = pi_row(lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      row[kk] = rr * T::kRowB + (((2 * kk + half) ^ bswz<D>(rr)) & (T::kCh - 1)) * 16;
+    const int g = lane >> 4, j = lane & 15;
+    const int ra = 8 * (g >> 1) + (j >> 2);
+    const int cc = 2 * (g & 1) + ((j & 3) >> 1), byte = 8 * (j & 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 4 * db + cc;
+      tlo[db] = ra * T::kRowB + ((c ^ bswz<D>(ra)) & (T::kCh - 1)) * 16 + byte;
+      thi[db] = (ra + 4) * T::kRowB + ((c ^ bswz<D>(ra + 4)) & (T::kCh - 1)) * 16 + byte;
+    }
+  }
+};
+
+// Order of the products inside one pipeline step: N1 score products and N2
+// gradient products, N1 = R N2, as R score products then one gradient
+// product, so consecutive products of one accumulator chain stay apart.
+template <int N1, int N2>
+__device__ constexpr bool op_is_grad(int i) {
+  if constexpr (N1 == 0) {
+    return true;
+  } else if constexpr (N2 == 0) {
+    return false;
+  } else {
+    constexpr int R = N1 / N2;
+    return i % (R + 1) == R;
+  }
+}
+template <int N1, int N2>
+__device__ constexpr int op_index(int i) {
+  if constexpr (N1 == 0 || N2 == 0) {
+    return i;
+  } else {
+    constexpr int R = N1 / N2;
+    return i % (R + 1) == R ? i / (R + 1) : (i / (R + 1)) * R + i % (R + 1);
+  }
+}
+
+// LDS reads feeding product i: one row-wise read or two transposed reads
+template <int N1, int N2>
+__device__ constexpr int ds_reads(int i) {
+  return i >= N1 + N2 ? 0 : (op_is_grad<N1, N2>(i) ? 2 : 1);
+}
+template <int N1, int N2>
+__device__ constexpr int ds_ahead() {
+  int n = 0;
+  for (int i = 0; i < kLook; ++i) n += ds_reads<N1, N2>(i);
+  return n;
+}
+// Pin the instruction order of one pipeline step: PRE other LDS reads and the
+// first kLook operand reads, then for every product the read kLook ahead, the
+// product, and VALU instructions of the probability block beside it.
+template <int N1, int N2, int VALU, int I>
+__device__ __forceinline__ void pin_product() {
+  constexpr int ds = ds_reads<N1, N2>(I + kLook);
+  if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+}
+template <int N1, int N2, int PRE, int VALU, int... I>
+__device__ __forceinline__ void pin_order(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE + ds_ahead<N1, N2>(), 0);
+  (pin_product<N1, N2, VALU, I>(), ...);
+}
+
+// Workgroup -> (batch*head unit, tile) over a grid of nbh * nt workgroups.
+// Workgroup i runs on XCD i % 8.  order > 0: tile 0 has the most work,
+// order < 0: the last tile has; then XCD x takes the units x, x + 8, ... and
+// starts the longest tiles of all of them first.  order == 0: equal tiles,
+// numbered so that each XCD holds whole units (their tiles share its L2).
+__device__ __forceinline__ void bwd_unit(int nbh, int nt, int order, int& bh, int& t) {
+  if (order != 0 && (nbh & 7) == 0) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3, hx = nbh >> 3;
+    const int r = k / hx;
+    bh = x + 8 * (k - r * hx);
+    t = order > 0 ? r : nt - 1 - r;
+  } else {
+    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = id / nt;
+    t = id - bh * nt;
+  }
+}
+
+// Element masks without scalar compares: bit c of the word is set iff
+// lo <= c <= hi (c = 16 (r / 8) + r % 8 in 0..31, the row or key offset of
+// accumulator register r inside its block), and an element is kept by
+// sign-extending its bit over the float.
+__device__ __forceinline__ uint32_t mask_word(int lo, int hi) {
+  const int l = max(lo, 0), h = min(hi, 31);
+  const uint32_t below_h = h < 0 ? 0u : (2u << h) - 1u;   // bits 0..h
+  const uint32_t below_l = l > 31 ? ~0u : (1u << l) - 1u;  // bits 0..l-1
+  return below_h & ~below_l;
+}
+__device__ __forceinline__ float keep_bit(uint32_t m, int c, float x) {
+  const uint32_t all = (uint32_t)((int)(m << (31 - c)) >> 31);
+  return __uint_as_float(__float_as_uint(x) & all);
+}
+
+template <bool B>
+using Bool = std::integral_constant<bool, B>;
+template <int I>
+using Int = std::integral_constant<int, I>;
 
 // ---------------------------------------------------------------- prep
 template <int D>
@@ -132,115 +296,234 @@ __global__ __launch_bounds__(kBThreads) void bwd_prep_kernel(BwdArgs a) {
     for (int j = 0; j < 4; ++j)
       s = fmaf(bf16_lo(x[j]), bf16_lo(y[j]), fmaf(bf16_hi(x[j]), bf16_hi(y[j]), s));
   }
-  a.ws_d[idx] = s;
-  a.ws_l2[idx] = a.lse[idx] * kLog2e;  // -inf (a row with no key) stays -inf
+  a.ws_nd[idx] = -s;
+  a.ws_nl[idx] = -a.lse[idx] / a.scale;  // +inf for a row with no key (always masked)
+}
+
+// Owner fragments: rows [r0, r0 + 32) of a [rows][heads][D] tensor (head base
+// g) as MFMA B operands, lane l32 = row, k-slots d = 16 kk + 8 h .. + 7; rows
+// past n read as zeros.
+template <int D>
+__device__ __forceinline__ void load_owner(bf16x8_t (&f)[D / 16], const uint16_t* g, long long rs,
+                                           int r0, int n, int lane) {
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const uint32_t nrec = (uint32_t)max(min(n - r0, kWaveRows), 0) * row_bytes;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g + (long long)max(r0, 0) * rs), 0, __builtin_amdgcn_readfirstlane(nrec), kRsrcWord3);
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2;
+    f[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
 template <int D>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int kRS = row_stride<D>();
-  __shared__ __attribute__((aligned(16))) char q_lds[kTile * kRS];
-  __shared__ __attribute__((aligned(16))) char g_lds[kTile * kRS];  // dO tile
-  __shared__ __attribute__((aligned(16))) float l2_lds[kTile];
-  __shared__ __attribute__((aligned(16))) float d_lds[kTile];
+  using T = BTile<D>;
+  constexpr int kSlot = 2 * T::kBytes + 2 * T::kVec;  // Q tile, dO tile, -lse/scale, -D
+  constexpr int kPer = 2 * T::kLoads + 1;             // DMA loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int H = a.heads, n_q = a.seqlen_q, n_k = a.seqlen_k, delta = n_k - n_q;
-  const int nkt = ceil_div(n_k, 4 * kWaveRows);
-  const int kt = blockIdx.x % nkt;
-  const int bh = blockIdx.x / nkt;
+  const int W = a.window_left;
+  const bool causal = a.causal != 0;
+  const int nkt = ceil_div(n_k, kUnit);
+  int bh, kt;
+  bwd_unit(a.batch * H, nkt, causal ? 1 : (W >= 0 ? -1 : 0), bh, kt);
   const int h = bh % H, b = bh / H;
   const long long rs = (long long)H * D;
-  const int k0 = kt * 4 * kWaveRows;
-  const int wk0 = k0 + wave * kWaveRows;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const int k0 = kt * kUnit, wk0 = k0 + wave * kWaveRows;
   const int key = wk0 + l32;  // this lane's key
 
-  // K^T and V^T operand fragments of this lane's key (rows past n_k are zero)
-  const uint16_t* kg = (const uint16_t*)a.k + ((long long)b * n_k * H + h) * D;
-  const uint16_t* vg = (const uint16_t*)a.v + ((long long)b * n_k * H + h) * D;
   bf16x8_t kf[D / 16], vf[D / 16];
-  {
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const uint32_t nrec = (uint32_t)max(min(n_k - wk0, kWaveRows), 0) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rk = rsrc_of(kg + (long long)max(wk0, 0) * rs, nrec);
-    const __amdgpu_buffer_rsrc_t rv = rsrc_of(vg + (long long)max(wk0, 0) * rs, nrec);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2;
-      kf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-  }
+  load_owner<D>(kf, (const uint16_t*)a.k + ((long long)b * n_k * H + h) * D, rs, wk0, n_k, lane);
+  load_owner<D>(vf, (const uint16_t*)a.v + ((long long)b * n_k * H + h) * D, rs, wk0, n_k, lane);
 
-  f32x16_t dkacc[D / 32], dvacc[D / 32];  // dK^T, dV^T: [d][key], lane = key
+  f32x16_t dk[D / 32], dv[D / 32];  // dK^T, dV^T: [d][key], lane = key
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      dkacc[db][r] = 0.0f;
-      dvacc[db][r] = 0.0f;
+      dk[db][r] = 0.0f;
+      dv[db][r] = 0.0f;
     }
 
-  // query rows that can see one of the workgroup's keys
+  // query rows that can see one of the workgroup's keys, in 64-row tiles
   int q_lo = 0, q_hi = n_q;
-  if (a.causal) q_lo = max(q_lo, k0 - delta);
-  if (a.window_left >= 0) q_hi = min(q_hi, k0 + 4 * kWaveRows - delta + a.window_left);
+  if (causal) q_lo = max(q_lo, k0 - delta);
+  if (W >= 0) q_hi = min(q_hi, k0 + kUnit - delta + W);
+  const int t_lo = q_lo / kTile;
+  const int nt = q_hi > q_lo ? ceil_div(q_hi, kTile) - t_lo : 0;
+
   const uint16_t* qg = (const uint16_t*)a.q + ((long long)b * n_q * H + h) * D;
   const uint16_t* gg = (const uint16_t*)a.dout + ((long long)b * n_q * H + h) * D;
-  const float* l2g = a.ws_l2 + ((long long)b * H + h) * n_q;
-  const float* dg = a.ws_d + ((long long)b * H + h) * n_q;
+  const float* nlg = a.ws_nl + ((long long)b * H + h) * n_q;
+  const float* ndg = a.ws_nd + ((long long)b * H + h) * n_q;
   const float c2 = a.scale_log2;
 
-  for (int q0 = (max(q_lo, 0) / kTile) * kTile; q0 < q_hi; q0 += kTile) {
-    stage_tile<D>(q_lds, qg, rs, q0, n_q, tid);
-    stage_tile<D>(g_lds, gg, rs, q0, n_q, tid);
-    if (tid < kTile) {
-      const int i = q0 + tid;
-      // rows past n_q: +inf makes P = 0 (they are masked anyway)
-      ((lds_float_t*)(lds_void_t*)l2_lds)[tid] = i < n_q ? l2g[i] : __builtin_inff();
-      ((lds_float_t*)(lds_void_t*)d_lds)[tid] = i < n_q ? dg[i] : 0.0f;
+  // DMA: wave w moves the 1 KB blocks w, w + 4, ... of each tensor's tile;
+  // lane l of block blk fills LDS position blk * 64 + l (row r, chunk slot p)
+  // with logical chunk p ^ bswz(r)
+  uint32_t xofs[T::kLoads];
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) {
+    const int s = (i * kBWaves + wave) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
+    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16);
+  }
+  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
+  auto issue = [&](int u) {
+    const int r0 = (t_lo + u) * kTile;
+    const uint32_t rows = (uint32_t)min(kTile, n_q - r0);
+    const u32x4_t rq = rsrc_of(qg + (long long)r0 * rs, rows * row_bytes);
+    const u32x4_t rg = rsrc_of(gg + (long long)r0 * rs, rows * row_bytes);
+    char* s = slot(u);
+#pragma unroll
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int blk = i * kBWaves + wave;
+      dma_b128(rq, xofs[i], lds_addr(s + blk * 1024));
+      dma_b128(rg, xofs[i], lds_addr(s + T::kBytes + blk * 1024));
     }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < kTile / 32; ++rb) {
-      f32x16_t sacc = {}, dpacc = {};
-      const int prow = rb * 32 + pi_row(l32);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(q_lds, prow, kk, half), kf[kk], sacc, 0, 0, 0);
-        dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(g_lds, prow, kk, half), vf[kk], dpacc, 0, 0, 0);
+    // waves 0, 2 load -lse/scale, waves 1, 3 load -D (the same values twice)
+    const u32x4_t rvec = rsrc_of((wave & 1) ? ndg + r0 : nlg + r0, rows * 4);
+    dma_b32(rvec, (uint32_t)lane * 4, lds_addr(s + 2 * T::kBytes + (wave & 1) * T::kVec));
+  };
+
+  const FragOffsets<D> fo(lane);
+  f32x16_t sacc[2], dpacc[2];  // [block parity]: S and dP of one 32-row block
+  bf16x8_t pf[2][2], sf[2][2];  // [block parity][16-row slice]: P and dS as B operands
+  auto block_row0 = [&](int j) { return (t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
+
+  // one pipeline step: the score products of block j + 1 (M1), the gradient
+  // products of block j - 1 (M2) and P, dS of block j (VV); P = j & 1
+  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, int j) {
+    constexpr bool kM1 = decltype(M1)::value, kM2 = decltype(M2)::value;
+    constexpr bool kVV = decltype(VV)::value, kMask = decltype(MASK)::value;
+    constexpr int p = decltype(PAR)::value;
+    constexpr int kN1 = kM1 ? 2 * (D / 16) : 0;
+    constexpr int kN2 = kM2 ? 4 * (D / 32) : 0;
+    constexpr int kN = kN1 + kN2;
+    // block j + 1 and j - 1 have parity 1 - p: row block 1 - p of their tile
+    const char* x1 = slot((j + 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
+    const char* x2 = slot((j - 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
+
+    auto fetch = [&](int i) -> bf16x8_t {
+      const int o = op_index<kN1, kN2>(i);
+      if (!op_is_grad<kN1, kN2>(i)) {
+        return lds_row(x1 + (o & 1) * T::kBytes + fo.row[o >> 1]);
+      } else {
+        const int ks = o / (2 * (D / 32)), rem = o % (2 * (D / 32)), db = rem >> 1;
+        const char* t = x2 + ((rem & 1) ? 0 : T::kBytes) + ks * 16 * T::kRowB;
+        return lds_tr(t + fo.tlo[db], t + fo.thi[db]);
       }
-      // register r of lane half h holds tile row rb*32 + 16 (r/8) + 8 h + r%8
-      bf16x8_t pf[2], sf[2];
+    };
+    // the score products of block j + 1 start from -lse/scale and -D of
+    // their rows: register r of half h is row 16 (r / 8) + 8 h + r % 8
+    f32x16_t nl_init, nd_init;
+    if constexpr (kM1) {
+      const char* vb = slot((j + 1) >> 1) + 2 * T::kBytes + (kWaveRows * (1 - p) + 8 * half) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int off = (q >> 1) * 64 + (q & 1) * 16;
+        const f32x4_t x = lds_f4(vb + off), y = lds_f4(vb + T::kVec + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          nl_init[4 * q + e] = x[e];
+          nd_init[4 * q + e] = y[e];
+        }
+      }
+    }
+    auto product = [&](int i, const bf16x8_t& f) {
+      const int o = op_index<kN1, kN2>(i);
+      if (!op_is_grad<kN1, kN2>(i)) {
+        const int kk = o >> 1;
+        if (o & 1) {
+          dpacc[1 - p] = mfma(f, vf[kk], kk == 0 ? nd_init : dpacc[1 - p]);
+        } else {
+          sacc[1 - p] = mfma(f, kf[kk], kk == 0 ? nl_init : sacc[1 - p]);
+        }
+      } else {
+        const int ks = o / (2 * (D / 32)), rem = o % (2 * (D / 32)), db = rem >> 1;
+        if (rem & 1) {
+          dk[db] = mfma(f, sf[1 - p][ks], dk[db]);
+        } else {
+          dv[db] = mfma(f, pf[1 - p][ks], dv[db]);
+        }
+      }
+    };
+
+    if constexpr (kVV) {
+      // sacc = S - lse / scale, dpacc = dP - D of block j
+      uint32_t keep = 0;
+      if constexpr (kMask) {
+        // key <= row + delta and key >= row + delta - W, row = r0 + 8 h + c
+        const int w = key - delta - block_row0(j) - 8 * half;
+        keep = mask_word(causal ? w : -kFar, W >= 0 ? w + W : kFar);
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int t0 = rb * 32 + 16 * ks + 8 * half;
-        float p[8], ds[8];
+        float pv[8], dsv[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float l2 = ((const lds_float_t*)(const lds_void_t*)l2_lds)[t0 + t];
-          const float dd = ((const lds_float_t*)(const lds_void_t*)d_lds)[t0 + t];
           const int r = 8 * ks + t;
-          const bool ok = allowed(a, q0 + t0 + t, key, delta);
-          p[t] = ok ? exp2_hw(fmaf(sacc[r], c2, -l2)) : 0.0f;
-          ds[t] = p[t] * (dpacc[r] - dd);
+          float e = exp2_hw(sacc[p][r] * c2);
+          if constexpr (kMask) e = keep_bit(keep, 16 * ks + t, e);
+          pv[t] = e;
+          dsv[t] = e * dpacc[p][r];
         }
-        pf[ks] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-        sf[ks] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+        pf[p][ks] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        sf[p][ks] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS over these 32 rows
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(g_lds, rb * 32 + 16 * ks, db, lane), pf[ks], dvacc[db], 0, 0, 0);
-          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(q_lds, rb * 32 + 16 * ks, db, lane), sf[ks], dkacc[db], 0, 0, 0);
-        }
     }
-    __syncthreads();
+
+    if constexpr (kN > 0) {
+      bf16x8_t fq[kLook + 1];
+#pragma unroll
+      for (int i = 0; i < kLook && i < kN; ++i) fq[i] = fetch(i);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        if (i + kLook < kN) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook);
+        product(i, fq[i % (kLook + 1)]);
+      }
+      pin_order<kN1, kN2, kM1 ? 8 : 0, kVV ? 2 : 0>(std::make_integer_sequence<int, kN>{});
+    }
+  };
+
+  if (nt > 0) {
+    issue(0);
+    if (nt > 1) issue(1);
+    if (nt > 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    barrier();
+    if (nt > 2) issue(2);
+    step(Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, Int<1>{}, -1);
+    step(Bool<true>{}, Bool<false>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 0);
+    // iteration u: tile u lands, then P, dS of blocks 2u - 1 and 2u.  Every
+    // block applies its element mask (all ones away from the mask edges):
+    // separate loops or branches for masked and unmasked blocks made the
+    // compiler spill the pipeline state to scratch
+    for (int u = 1; u < nt; ++u) {
+      // tile u has landed once at most the loads of tile u + 1 are in flight
+      if (u + 1 < nt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      barrier();  // tile u visible; every wave is done with tile u - 2
+      if (u + 2 < nt) issue(u + 2);
+      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * u - 1);
+      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 2 * u);
+    }
+    step(Bool<false>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * nt - 1);
+    step(Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, Int<0>{}, 2 * nt);
   }
 
   // lane holds d = 32 db + 8 (r/4) + 4 h + r%4 of its key
@@ -253,10 +536,10 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + half * 4;
         u32x2_t pk, pv;
-        pk[0] = pack_bf16x2(a.scale * dkacc[db][g4 * 4 + 0], a.scale * dkacc[db][g4 * 4 + 1]);
-        pk[1] = pack_bf16x2(a.scale * dkacc[db][g4 * 4 + 2], a.scale * dkacc[db][g4 * 4 + 3]);
-        pv[0] = pack_bf16x2(dvacc[db][g4 * 4 + 0], dvacc[db][g4 * 4 + 1]);
-        pv[1] = pack_bf16x2(dvacc[db][g4 * 4 + 2], dvacc[db][g4 * 4 + 3]);
+        pk[0] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 0], a.scale * dk[db][g4 * 4 + 1]);
+        pk[1] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 2], a.scale * dk[db][g4 * 4 + 3]);
+        pv[0] = pack_bf16x2(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]);
+        pv[1] = pack_bf16x2(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]);
         *(u32x2_t*)(dkp + d) = pk;
         *(u32x2_t*)(dvp + d) = pv;
       }
@@ -266,97 +549,176 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dQ
 template <int D>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int kRS = row_stride<D>();
-  __shared__ __attribute__((aligned(16))) char k_lds[kTile * kRS];
-  __shared__ __attribute__((aligned(16))) char v_lds[kTile * kRS];
+  using T = BTile<D>;
+  constexpr int kSlot = 2 * T::kBytes;  // K tile, V tile
+  constexpr int kPer = 2 * T::kLoads;
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int H = a.heads, n_q = a.seqlen_q, n_k = a.seqlen_k, delta = n_k - n_q;
-  const int nqt = ceil_div(n_q, 4 * kWaveRows);
-  const int qt = blockIdx.x % nqt;
-  const int bh = blockIdx.x / nqt;
+  const int W = a.window_left;
+  const bool causal = a.causal != 0;
+  const int nqt = ceil_div(n_q, kUnit);
+  int bh, qt;
+  bwd_unit(a.batch * H, nqt, causal ? -1 : (W >= 0 ? 1 : 0), bh, qt);
   const int h = bh % H, b = bh / H;
   const long long rs = (long long)H * D;
-  const int q0 = qt * 4 * kWaveRows;
-  const int wq0 = q0 + wave * kWaveRows;
+  const uint32_t row_bytes = (uint32_t)(rs * 2);
+  const int q0 = qt * kUnit, wq0 = q0 + wave * kWaveRows;
   const int row = wq0 + l32;  // this lane's query row
 
-  // Q^T and dO^T operand fragments of this lane's row (rows past n_q are zero)
-  const uint16_t* qg = (const uint16_t*)a.q + ((long long)b * n_q * H + h) * D;
-  const uint16_t* gg = (const uint16_t*)a.dout + ((long long)b * n_q * H + h) * D;
   bf16x8_t qf[D / 16], gf[D / 16];
-  {
-    const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, kWaveRows), 0) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rq = rsrc_of(qg + (long long)max(wq0, 0) * rs, nrec);
-    const __amdgpu_buffer_rsrc_t rg = rsrc_of(gg + (long long)max(wq0, 0) * rs, nrec);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2;
-      qf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      gf[kk] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
-    }
-  }
+  load_owner<D>(qf, (const uint16_t*)a.q + ((long long)b * n_q * H + h) * D, rs, wq0, n_q, lane);
+  load_owner<D>(gf, (const uint16_t*)a.dout + ((long long)b * n_q * H + h) * D, rs, wq0, n_q, lane);
   const bool row_live = row < n_q;
-  const float l2 = row_live ? a.ws_l2[((long long)b * H + h) * n_q + row] : __builtin_inff();
-  const float dd = row_live ? a.ws_d[((long long)b * H + h) * n_q + row] : 0.0f;
+  // exp2 argument offset (-lse * log2 e) and -D of this lane's row; rows past
+  // n_q get probability 0
+  const float nlc = row_live ? a.ws_nl[((long long)b * H + h) * n_q + row] * a.scale_log2
+                             : -__builtin_inff();
+  const float nd = row_live ? a.ws_nd[((long long)b * H + h) * n_q + row] : 0.0f;
 
-  f32x16_t dqacc[D / 32];  // dQ^T: [d][row], lane = row
+  f32x16_t dq[D / 32];  // dQ^T: [d][row], lane = row
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
 
-  // keys the workgroup's rows can see
-  const int q_last = min(q0 + 4 * kWaveRows, n_q) - 1;
+  // keys the workgroup's rows can see, in 64-key tiles
+  const int q_last = min(q0 + kUnit, n_q) - 1;
   int k_lo = 0, k_hi = n_k;
-  if (a.causal) k_hi = min(k_hi, q_last + delta + 1);
-  if (a.window_left >= 0) k_lo = max(k_lo, q0 + delta - a.window_left);
+  if (causal) k_hi = min(k_hi, q_last + delta + 1);
+  if (W >= 0) k_lo = max(k_lo, q0 + delta - W);
+  const int t_lo = k_lo / kTile;
+  const int nt = k_hi > k_lo ? ceil_div(k_hi, kTile) - t_lo : 0;
+
   const uint16_t* kg = (const uint16_t*)a.k + ((long long)b * n_k * H + h) * D;
   const uint16_t* vg = (const uint16_t*)a.v + ((long long)b * n_k * H + h) * D;
   const float c2 = a.scale_log2;
 
-  for (int k0 = (max(k_lo, 0) / kTile) * kTile; k0 < k_hi; k0 += kTile) {
-    stage_tile<D>(k_lds, kg, rs, k0, n_k, tid);
-    stage_tile<D>(v_lds, vg, rs, k0, n_k, tid);
-    __syncthreads();
-    f32x16_t sacc[kTile / 32], dpacc[kTile / 32];
+  uint32_t xofs[T::kLoads];
 #pragma unroll
-    for (int kb = 0; kb < kTile / 32; ++kb) {
-      sacc[kb] = f32x16_t{};
-      dpacc[kb] = f32x16_t{};
-      const int prow = kb * 32 + pi_row(l32);
+  for (int i = 0; i < T::kLoads; ++i) {
+    const int s = (i * kBWaves + wave) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
+    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16);
+  }
+  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
+  auto issue = [&](int u) {
+    const int r0 = (t_lo + u) * kTile;
+    const uint32_t rows = (uint32_t)min(kTile, n_k - r0);
+    const u32x4_t rk = rsrc_of(kg + (long long)r0 * rs, rows * row_bytes);
+    const u32x4_t rv = rsrc_of(vg + (long long)r0 * rs, rows * row_bytes);
+    char* s = slot(u);
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(k_lds, prow, kk, half), qf[kk], sacc[kb], 0, 0, 0);
-        dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(v_lds, prow, kk, half), gf[kk], dpacc[kb], 0, 0, 0);
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int blk = i * kBWaves + wave;
+      dma_b128(rk, xofs[i], lds_addr(s + blk * 1024));
+      dma_b128(rv, xofs[i], lds_addr(s + T::kBytes + blk * 1024));
+    }
+  };
+
+  const FragOffsets<D> fo(lane);
+  f32x16_t sacc[2], dpacc[2];  // [block parity]: S^T and dP^T of one 32-key block
+  bf16x8_t sf[2][2];            // [block parity][16-key slice]: dS^T as B operand
+  auto block_key0 = [&](int j) { return (t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
+
+  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, int j) {
+    constexpr bool kM1 = decltype(M1)::value, kM2 = decltype(M2)::value;
+    constexpr bool kVV = decltype(VV)::value, kMask = decltype(MASK)::value;
+    constexpr int p = decltype(PAR)::value;
+    constexpr int kN1 = kM1 ? 2 * (D / 16) : 0;
+    constexpr int kN2 = kM2 ? 2 * (D / 32) : 0;
+    constexpr int kN = kN1 + kN2;
+    const char* x1 = slot((j + 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
+    const char* x2 = slot((j - 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
+
+    auto fetch = [&](int i) -> bf16x8_t {
+      const int o = op_index<kN1, kN2>(i);
+      if (!op_is_grad<kN1, kN2>(i)) {
+        return lds_row(x1 + (o & 1) * T::kBytes + fo.row[o >> 1]);
+      } else {
+        const int ks = o / (D / 32), db = o % (D / 32);
+        const char* t = x2 + ks * 16 * T::kRowB;
+        return lds_tr(t + fo.tlo[db], t + fo.thi[db]);
+      }
+    };
+    auto product = [&](int i, const bf16x8_t& f) {
+      const int o = op_index<kN1, kN2>(i);
+      if (!op_is_grad<kN1, kN2>(i)) {
+        const int kk = o >> 1;
+        if (o & 1) {
+          dpacc[1 - p] = mfma(f, gf[kk], kk == 0 ? f32x16_t{} : dpacc[1 - p]);
+        } else {
+          sacc[1 - p] = mfma(f, qf[kk], kk == 0 ? f32x16_t{} : sacc[1 - p]);
+        }
+      } else {
+        const int ks = o / (D / 32), db = o % (D / 32);
+        dq[db] = mfma(f, sf[1 - p][ks], dq[db]);
+      }
+    };
+
+    if constexpr (kVV) {
+      uint32_t keep = 0;
+      if constexpr (kMask) {
+        // key = k0 + 8 h + c: key < n_k, key <= row + delta, key >= row + delta - W
+        const int base = block_key0(j) + 8 * half;
+        const int v = row + delta - base;
+        keep = mask_word(W >= 0 ? v - W : -kFar, causal ? min(n_k - 1 - base, v) : n_k - 1 - base);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        float dsv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int r = 8 * ks + t;
+          float e = exp2_hw(fmaf(sacc[p][r], c2, nlc));
+          if constexpr (kMask) e = keep_bit(keep, 16 * ks + t, e);
+          dsv[t] = e * (dpacc[p][r] + nd);
+        }
+        sf[p][ks] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
       }
     }
-    // register r of lane half h holds key k0 + 32 kb + 16 (r/8) + 8 h + r%8
-    bf16x8_t sf[kTile / 16];
+
+    if constexpr (kN > 0) {
+      bf16x8_t fq[kLook + 1];
 #pragma unroll
-    for (int ks = 0; ks < kTile / 16; ++ks) {
-      const int kb = ks >> 1, o8 = (ks & 1) * 8;
-      float ds[8];
+      for (int i = 0; i < kLook && i < kN; ++i) fq[i] = fetch(i);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int r = o8 + t;
-        const int key = k0 + 32 * kb + 16 * (r >> 3) + 8 * half + (r & 7);
-        const bool ok = allowed(a, row, key, delta);
-        const float p = ok ? exp2_hw(fmaf(sacc[kb][r], c2, -l2)) : 0.0f;
-        ds[t] = p * (dpacc[kb][r] - dd);
+      for (int i = 0; i < kN; ++i) {
+        if (i + kLook < kN) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook);
+        product(i, fq[i % (kLook + 1)]);
       }
-      sf[ks] = to_bf16x8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+      pin_order<kN1, kN2, 0, kVV ? 2 : 0>(std::make_integer_sequence<int, kN>{});
     }
-    // dQ^T += K^T dS^T over these keys
-#pragma unroll
-    for (int ks = 0; ks < kTile / 16; ++ks)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(k_lds, 16 * ks, db, lane), sf[ks], dqacc[db], 0, 0, 0);
-    __syncthreads();
+  };
+
+  if (nt > 0) {
+    issue(0);
+    if (nt > 1) issue(1);
+    if (nt > 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    barrier();
+    if (nt > 2) issue(2);
+    step(Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, Int<1>{}, -1);
+    step(Bool<true>{}, Bool<false>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 0);
+    // every block applies its element mask, as in the dK, dV kernel
+    for (int u = 1; u < nt; ++u) {
+      if (u + 1 < nt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      barrier();
+      if (u + 2 < nt) issue(u + 2);
+      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * u - 1);
+      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 2 * u);
+    }
+    step(Bool<false>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * nt - 1);
+    step(Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, Int<0>{}, 2 * nt);
   }
 
   if (row_live) {
@@ -367,8 +729,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + half * 4;
         u32x2_t pq;
-        pq[0] = pack_bf16x2(a.scale * dqacc[db][g4 * 4 + 0], a.scale * dqacc[db][g4 * 4 + 1]);
-        pq[1] = pack_bf16x2(a.scale * dqacc[db][g4 * 4 + 2], a.scale * dqacc[db][g4 * 4 + 3]);
+        pq[0] = pack_bf16x2(a.scale * dq[db][g4 * 4 + 0], a.scale * dq[db][g4 * 4 + 1]);
+        pq[1] = pack_bf16x2(a.scale * dq[db][g4 * 4 + 2], a.scale * dq[db][g4 * 4 + 3]);
         *(u32x2_t*)(qp + d) = pq;
       }
   }
@@ -378,8 +740,8 @@ template <int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.batch * a.heads * a.seqlen_q;
   const long long g0 = (rows + kBThreads - 1) / kBThreads;
-  const long long g1 = (long long)a.batch * a.heads * ceil_div(a.seqlen_k, 4 * kWaveRows);
-  const long long g2 = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, 4 * kWaveRows);
+  const long long g1 = (long long)a.batch * a.heads * ceil_div(a.seqlen_k, kUnit);
+  const long long g2 = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, kUnit);
   if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidValue;
   if (g0 > 0) {
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)g0), dim3(kBThreads), 0, stream, a);

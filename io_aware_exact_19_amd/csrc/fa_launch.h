@@ -63,8 +63,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* ws_d;         // [batch, heads, seqlen_q] rowsum(dO o O)
-  float* ws_l2;        // [batch, heads, seqlen_q] lse * log2(e)
+  float* ws_nd;        // [batch, heads, seqlen_q] -rowsum(dO o O)
+  float* ws_nl;        // [batch, heads, seqlen_q] -lse / scale (score units)
   int batch;
   int heads;
   int seqlen_q;
