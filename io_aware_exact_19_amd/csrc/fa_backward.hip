@@ -40,7 +40,6 @@
 #include "fa_launch.h"
 
 #include <type_traits>
-#include <utility>
 
 namespace fa {
 namespace {
@@ -133,6 +132,26 @@ __device__ __forceinline__ void dma_b32(const u32x4_t& rs, uint32_t voff, uint32
       : "memory");
 }
 
+// Four 16-byte-per-lane loads into four consecutive 1 KB LDS blocks under one
+// M0 setting: the instruction offset (k * 1024) moves the LDS destination and
+// the memory address together, so voff[k] carries the memory offset minus it.
+__device__ __forceinline__ void dma_b128x4(const u32x4_t& rs, uint32_t v0, uint32_t v1, uint32_t v2,
+                                           uint32_t v3, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rs), "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)p);
 }
@@ -152,6 +171,17 @@ __device__ __forceinline__ bf16x8_t lds_tr(const char* lo, const char* hi) {
 }
 __device__ __forceinline__ f32x4_t lds_f4(const char* p) {
   return *(const lds_f32x4_t*)((const lds_void_t*)p);
+}
+
+// Anchor a value at this point of the program: the optimizer may not sink its
+// computation past here (sched_barrier alone binds only the final scheduler)
+__device__ __forceinline__ void anchor(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void anchor(uint32_t x) { asm volatile("" ::"v"(x)); }
+
+// two floats to a bf16 pair (round to nearest even) in one conversion
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2v_t));
 }
 
 __device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
@@ -211,33 +241,6 @@ __device__ constexpr int op_index(int i) {
   }
 }
 
-// LDS reads feeding product i: one row-wise read or two transposed reads
-template <int N1, int N2>
-__device__ constexpr int ds_reads(int i) {
-  return i >= N1 + N2 ? 0 : (op_is_grad<N1, N2>(i) ? 2 : 1);
-}
-template <int N1, int N2>
-__device__ constexpr int ds_ahead() {
-  int n = 0;
-  for (int i = 0; i < kLook; ++i) n += ds_reads<N1, N2>(i);
-  return n;
-}
-// Pin the instruction order of one pipeline step: PRE other LDS reads and the
-// first kLook operand reads, then for every product the read kLook ahead, the
-// product, and VALU instructions of the probability block beside it.
-template <int N1, int N2, int VALU, int I>
-__device__ __forceinline__ void pin_product() {
-  constexpr int ds = ds_reads<N1, N2>(I + kLook);
-  if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  if constexpr (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-}
-template <int N1, int N2, int PRE, int VALU, int... I>
-__device__ __forceinline__ void pin_order(std::integer_sequence<int, I...>) {
-  __builtin_amdgcn_sched_group_barrier(0x100, PRE + ds_ahead<N1, N2>(), 0);
-  (pin_product<N1, N2, VALU, I>(), ...);
-}
-
 // Workgroup -> (batch*head unit, tile) over a grid of nbh * nt workgroups.
 // Workgroup i runs on XCD i % 8.  order > 0: tile 0 has the most work,
 // order < 0: the last tile has; then XCD x takes the units x, x + 8, ... and
@@ -270,6 +273,15 @@ __device__ __forceinline__ float keep_bit(uint32_t m, int c, float x) {
   const uint32_t all = (uint32_t)((int)(m << (31 - c)) >> 31);
   return __uint_as_float(__float_as_uint(x) & all);
 }
+
+// Buffer descriptors and LDS slot of one tile's DMA.  Tiles past the last
+// get descriptors of size 0: their loads fetch nothing and write zeros into a
+// free ring slot, so every iteration issues the same number of loads and the
+// waits use one constant count.
+struct DmaTile {
+  u32x4_t x, y, vec;
+  char* lds;
+};
 
 template <bool B>
 using Bool = std::integral_constant<bool, B>;
@@ -324,6 +336,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using T = BTile<D>;
   constexpr int kSlot = 2 * T::kBytes + 2 * T::kVec;  // Q tile, dO tile, -lse/scale, -D
   constexpr int kPer = 2 * T::kLoads + 1;             // DMA loads per wave per tile
+  constexpr int kPieces = 3;                          // Q group, dO group, vector
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -367,43 +380,69 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float* ndg = a.ws_nd + ((long long)b * H + h) * n_q;
   const float c2 = a.scale_log2;
 
-  // DMA: wave w moves the 1 KB blocks w, w + 4, ... of each tensor's tile;
+  // DMA: wave w moves the 1 KB blocks 4w .. 4w + 3 of each tensor's tile;
   // lane l of block blk fills LDS position blk * 64 + l (row r, chunk slot p)
-  // with logical chunk p ^ bswz(r)
+  // with logical chunk p ^ bswz(r).  xofs[i] is that memory offset minus the
+  // instruction offset i * 1024 of block 4w + i (see dma_b128x4).
+  static_assert(T::kLoads == 4 || T::kLoads == 2, "DMA grouping");
   uint32_t xofs[T::kLoads];
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
-    const int s = (i * kBWaves + wave) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
-    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16);
+    const int s = (wave * T::kLoads + i) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
+    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16) -
+              (uint32_t)(i * 1024);
   }
-  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
-  auto issue = [&](int u) {
-    const int r0 = (t_lo + u) * kTile;
-    const uint32_t rows = (uint32_t)min(kTile, n_q - r0);
-    const u32x4_t rq = rsrc_of(qg + (long long)r0 * rs, rows * row_bytes);
-    const u32x4_t rg = rsrc_of(gg + (long long)r0 * rs, rows * row_bytes);
-    char* s = slot(u);
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-      const int blk = i * kBWaves + wave;
-      dma_b128(rq, xofs[i], lds_addr(s + blk * 1024));
-      dma_b128(rg, xofs[i], lds_addr(s + T::kBytes + blk * 1024));
+  // this wave's blocks of one tensor's tile
+  auto dma_group = [&](const u32x4_t& rsrc, uint32_t lds_base) {
+    if constexpr (T::kLoads == 4) {
+      dma_b128x4(rsrc, xofs[0], xofs[1], xofs[2], xofs[3], lds_base);
+    } else {
+      dma_b128(rsrc, xofs[0], lds_base);
+      dma_b128(rsrc, xofs[1] + 1024, lds_base + 1024);
     }
+  };
+  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
+  auto dma_setup = [&](int u) {
+    DmaTile t;
+    const int r0 = u < nt ? (t_lo + u) * kTile : 0;
+    const uint32_t rows = u < nt ? (uint32_t)min(kTile, n_q - r0) : 0u;
+    t.x = rsrc_of(qg + (long long)r0 * rs, rows * row_bytes);
+    t.y = rsrc_of(gg + (long long)r0 * rs, rows * row_bytes);
     // waves 0, 2 load -lse/scale, waves 1, 3 load -D (the same values twice)
-    const u32x4_t rvec = rsrc_of((wave & 1) ? ndg + r0 : nlg + r0, rows * 4);
-    dma_b32(rvec, (uint32_t)lane * 4, lds_addr(s + 2 * T::kBytes + (wave & 1) * T::kVec));
+    t.vec = rsrc_of((wave & 1) ? ndg + r0 : nlg + r0, rows * 4);
+    t.lds = slot(u);
+    return t;
+  };
+  auto dma_piece = [&](const DmaTile& t, int k) {
+    if (k < 2) {
+      dma_group(k == 0 ? t.x : t.y, lds_addr(t.lds + k * T::kBytes + wave * T::kLoads * 1024));
+    } else {
+      dma_b32(t.vec, (uint32_t)lane * 4, lds_addr(t.lds + 2 * T::kBytes + (wave & 1) * T::kVec));
+    }
   };
 
   const FragOffsets<D> fo(lane);
   f32x16_t sacc[2], dpacc[2];  // [block parity]: S and dP of one 32-row block
   bf16x8_t pf[2][2], sf[2][2];  // [block parity][16-row slice]: P and dS as B operands
   auto block_row0 = [&](int j) { return (t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
+  auto block_masked = [&](int j) {
+    const int r0 = block_row0(j);
+    return (causal && wk0 + kWaveRows - 1 > r0 + delta) ||
+           (W >= 0 && wk0 < r0 + kWaveRows - 1 + delta - W);
+  };
 
   // one pipeline step: the score products of block j + 1 (M1), the gradient
-  // products of block j - 1 (M2) and P, dS of block j (VV); P = j & 1
-  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, int j) {
+  // products of block j - 1 (M2), P and dS of block j (VV), and with DMA the
+  // loads of one later tile; PAR = j & 1.  The step is a sequence of chunks,
+  // one per product: its operand reads kLook products ahead, the product, a
+  // share of the probability work and of the loads.  sched_barrier keeps the
+  // chunks in this order, so the vector work runs beside the matrix pipe
+  // instead of after it (one wave per SIMD: nothing else would fill it).
+  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, auto DMA, const DmaTile& dt,
+                  int j) {
     constexpr bool kM1 = decltype(M1)::value, kM2 = decltype(M2)::value;
     constexpr bool kVV = decltype(VV)::value, kMask = decltype(MASK)::value;
+    constexpr bool kDma = decltype(DMA)::value;
     constexpr int p = decltype(PAR)::value;
     constexpr int kN1 = kM1 ? 2 * (D / 16) : 0;
     constexpr int kN2 = kM2 ? 4 * (D / 32) : 0;
@@ -457,29 +496,46 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    if constexpr (kVV) {
-      // sacc = S - lse / scale, dpacc = dP - D of block j
-      uint32_t keep = 0;
-      if constexpr (kMask) {
-        // key <= row + delta and key >= row + delta - W, row = r0 + 8 h + c
-        const int w = key - delta - block_row0(j) - 8 * half;
-        keep = mask_word(causal ? w : -kFar, W >= 0 ? w + W : kFar);
+    // P and dS of block j from sacc = S - lse / scale, dpacc = dP - D, in
+    // 32 pieces: pieces 0..15 exponentiate register q, pieces 16..31 form dS
+    // of register q - 16 and pack pairs to bf16
+    float ev[16], dsv[16];
+    uint32_t pw[8], sw[8];
+    auto vpiece = [&](int q) {
+      if (q < 16) {
+        ev[q] = exp2_hw(sacc[p][q] * c2);
+        anchor(ev[q]);
+      } else {
+        const int t = q - 16;
+        dsv[t] = ev[t] * dpacc[p][t];
+        if (t & 1) {
+          pw[t >> 1] = pack2(ev[t - 1], ev[t]);
+          sw[t >> 1] = pack2(dsv[t - 1], dsv[t]);
+          anchor(pw[t >> 1]);
+          anchor(sw[t >> 1]);
+        }
       }
+    };
+    // the same with the causal / window mask (pairs outside the band get 0),
+    // for the few blocks that cross a mask edge
+    auto probs_masked = [&]() {
+      // key <= row + delta and key >= row + delta - W, row = r0 + 8 h + c
+      const int w = key - delta - block_row0(j) - 8 * half;
+      const uint32_t keep = mask_word(causal ? w : -kFar, W >= 0 ? w + W : kFar);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float pv[8], dsv[8];
+        float pv[8], dv8[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int r = 8 * ks + t;
-          float e = exp2_hw(sacc[p][r] * c2);
-          if constexpr (kMask) e = keep_bit(keep, 16 * ks + t, e);
+          const float e = keep_bit(keep, 16 * ks + t, exp2_hw(sacc[p][r] * c2));
           pv[t] = e;
-          dsv[t] = e * dpacc[p][r];
+          dv8[t] = e * dpacc[p][r];
         }
         pf[p][ks] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-        sf[p][ks] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        sf[p][ks] = to_bf16x8(dv8[0], dv8[1], dv8[2], dv8[3], dv8[4], dv8[5], dv8[6], dv8[7]);
       }
-    }
+    };
 
     if constexpr (kN > 0) {
       bf16x8_t fq[kLook + 1];
@@ -489,41 +545,59 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int i = 0; i < kN; ++i) {
         if (i + kLook < kN) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook);
         product(i, fq[i % (kLook + 1)]);
+        if constexpr (kVV) {
+#pragma unroll
+          for (int q = i * 32 / kN; q < (i + 1) * 32 / kN; ++q) vpiece(q);
+        }
+        if constexpr (kDma) {
+#pragma unroll
+          for (int k = 0; k < kPieces; ++k)
+            if (k * kN / kPieces + kN / (2 * kPieces) == i) dma_piece(dt, k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      pin_order<kN1, kN2, kM1 ? 8 : 0, kVV ? 2 : 0>(std::make_integer_sequence<int, kN>{});
+    }
+    if constexpr (kVV) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[p][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
+        sf[p][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{sw[4 * ks], sw[4 * ks + 1], sw[4 * ks + 2], sw[4 * ks + 3]});
+      }
+      // blocks that cross a mask edge redo P and dS with the mask after the
+      // step's products (their inputs stay intact until the next step)
+      if constexpr (kMask) {
+        if (block_masked(j)) probs_masked();
+      }
     }
   };
 
   if (nt > 0) {
-    issue(0);
-    if (nt > 1) issue(1);
-    if (nt > 1) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    constexpr Bool<true> y{};
+    constexpr Bool<false> n{};
+    {
+      const DmaTile t0 = dma_setup(0), t1 = dma_setup(1);
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) dma_piece(t0, k);
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) dma_piece(t1, k);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));  // tile 0 has landed
     barrier();
-    if (nt > 2) issue(2);
-    step(Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, Int<1>{}, -1);
-    step(Bool<true>{}, Bool<false>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 0);
-    // iteration u: tile u lands, then P, dS of blocks 2u - 1 and 2u.  Every
-    // block applies its element mask (all ones away from the mask edges):
-    // separate loops or branches for masked and unmasked blocks made the
-    // compiler spill the pipeline state to scratch
+    step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
+    step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
+    // iteration u: tile u lands, then P, dS of blocks 2u - 1 and 2u while the
+    // loads of tile u + 2 go out (one loop: separate loops for masked and
+    // unmasked blocks made the compiler spill the pipeline state to scratch)
     for (int u = 1; u < nt; ++u) {
       // tile u has landed once at most the loads of tile u + 1 are in flight
-      if (u + 1 < nt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
       barrier();  // tile u visible; every wave is done with tile u - 2
-      if (u + 2 < nt) issue(u + 2);
-      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * u - 1);
-      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 2 * u);
+      step(y, y, y, y, Int<1>{}, y, dma_setup(u + 2), 2 * u - 1);
+      step(y, y, y, y, Int<0>{}, n, DmaTile{}, 2 * u);
     }
-    step(Bool<false>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * nt - 1);
-    step(Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, Int<0>{}, 2 * nt);
+    step(n, y, y, y, Int<1>{}, n, DmaTile{}, 2 * nt - 1);
+    step(n, y, n, n, Int<0>{}, n, DmaTile{}, 2 * nt);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the size-0 loads of the last tiles
   }
 
   // lane holds d = 32 db + 8 (r/4) + 4 h + r%4 of its key
@@ -551,7 +625,8 @@ template <int D>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using T = BTile<D>;
   constexpr int kSlot = 2 * T::kBytes;  // K tile, V tile
-  constexpr int kPer = 2 * T::kLoads;
+  constexpr int kPer = 2 * T::kLoads;  // DMA loads per wave per tile
+  constexpr int kPieces = 2;           // K group, V group
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -597,35 +672,52 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* vg = (const uint16_t*)a.v + ((long long)b * n_k * H + h) * D;
   const float c2 = a.scale_log2;
 
-  uint32_t xofs[T::kLoads];
+  uint32_t xofs[T::kLoads];  // as in the dK, dV kernel
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
-    const int s = (i * kBWaves + wave) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
-    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16);
+    const int s = (wave * T::kLoads + i) * 64 + lane, r = s / T::kCh, p = s % T::kCh;
+    xofs[i] = (uint32_t)r * row_bytes + (uint32_t)(((p ^ bswz<D>(r)) & (T::kCh - 1)) * 16) -
+              (uint32_t)(i * 1024);
   }
-  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
-  auto issue = [&](int u) {
-    const int r0 = (t_lo + u) * kTile;
-    const uint32_t rows = (uint32_t)min(kTile, n_k - r0);
-    const u32x4_t rk = rsrc_of(kg + (long long)r0 * rs, rows * row_bytes);
-    const u32x4_t rv = rsrc_of(vg + (long long)r0 * rs, rows * row_bytes);
-    char* s = slot(u);
-#pragma unroll
-    for (int i = 0; i < T::kLoads; ++i) {
-      const int blk = i * kBWaves + wave;
-      dma_b128(rk, xofs[i], lds_addr(s + blk * 1024));
-      dma_b128(rv, xofs[i], lds_addr(s + T::kBytes + blk * 1024));
+  // this wave's blocks of one tensor's tile
+  auto dma_group = [&](const u32x4_t& rsrc, uint32_t lds_base) {
+    if constexpr (T::kLoads == 4) {
+      dma_b128x4(rsrc, xofs[0], xofs[1], xofs[2], xofs[3], lds_base);
+    } else {
+      dma_b128(rsrc, xofs[0], lds_base);
+      dma_b128(rsrc, xofs[1] + 1024, lds_base + 1024);
     }
+  };
+  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
+  auto dma_setup = [&](int u) {
+    DmaTile t;
+    const int r0 = u < nt ? (t_lo + u) * kTile : 0;
+    const uint32_t rows = u < nt ? (uint32_t)min(kTile, n_k - r0) : 0u;
+    t.x = rsrc_of(kg + (long long)r0 * rs, rows * row_bytes);
+    t.y = rsrc_of(vg + (long long)r0 * rs, rows * row_bytes);
+    t.lds = slot(u);
+    return t;
+  };
+  auto dma_piece = [&](const DmaTile& t, int k) {
+    dma_group(k == 0 ? t.x : t.y, lds_addr(t.lds + k * T::kBytes + wave * T::kLoads * 1024));
   };
 
   const FragOffsets<D> fo(lane);
   f32x16_t sacc[2], dpacc[2];  // [block parity]: S^T and dP^T of one 32-key block
   bf16x8_t sf[2][2];            // [block parity][16-key slice]: dS^T as B operand
   auto block_key0 = [&](int j) { return (t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
+  auto block_masked = [&](int j) {
+    const int k0 = block_key0(j);
+    return k0 + kWaveRows > n_k || (causal && k0 + kWaveRows - 1 > wq0 + delta) ||
+           (W >= 0 && k0 < wq0 + kWaveRows - 1 + delta - W);
+  };
 
-  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, int j) {
+  // one pipeline step, chunked as in the dK, dV kernel
+  auto step = [&](auto M1, auto M2, auto VV, auto MASK, auto PAR, auto DMA, const DmaTile& dt,
+                  int j) {
     constexpr bool kM1 = decltype(M1)::value, kM2 = decltype(M2)::value;
     constexpr bool kVV = decltype(VV)::value, kMask = decltype(MASK)::value;
+    constexpr bool kDma = decltype(DMA)::value;
     constexpr int p = decltype(PAR)::value;
     constexpr int kN1 = kM1 ? 2 * (D / 16) : 0;
     constexpr int kN2 = kM2 ? 2 * (D / 32) : 0;
@@ -658,27 +750,42 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       }
     };
 
-    if constexpr (kVV) {
-      uint32_t keep = 0;
-      if constexpr (kMask) {
-        // key = k0 + 8 h + c: key < n_k, key <= row + delta, key >= row + delta - W
-        const int base = block_key0(j) + 8 * half;
-        const int v = row + delta - base;
-        keep = mask_word(W >= 0 ? v - W : -kFar, causal ? min(n_k - 1 - base, v) : n_k - 1 - base);
+    // dS^T of block j in 32 pieces: 0..15 exponentiate register q, 16..31
+    // form dS of register q - 16 and pack pairs to bf16
+    float ev[16], dsv[16];
+    uint32_t sw[8];
+    auto vpiece = [&](int q) {
+      if (q < 16) {
+        ev[q] = exp2_hw(fmaf(sacc[p][q], c2, nlc));
+        anchor(ev[q]);
+      } else {
+        const int t = q - 16;
+        dsv[t] = ev[t] * (dpacc[p][t] + nd);
+        if (t & 1) {
+          sw[t >> 1] = pack2(dsv[t - 1], dsv[t]);
+          anchor(sw[t >> 1]);
+        }
       }
+    };
+    // with the mask: keys outside the band or past n_k get 0
+    auto probs_masked = [&]() {
+      // key = k0 + 8 h + c: key < n_k, key <= row + delta, key >= row + delta - W
+      const int base = block_key0(j) + 8 * half;
+      const int v = row + delta - base;
+      const uint32_t keep =
+          mask_word(W >= 0 ? v - W : -kFar, causal ? min(n_k - 1 - base, v) : n_k - 1 - base);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        float dsv[8];
+        float d8[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
           const int r = 8 * ks + t;
-          float e = exp2_hw(fmaf(sacc[p][r], c2, nlc));
-          if constexpr (kMask) e = keep_bit(keep, 16 * ks + t, e);
-          dsv[t] = e * (dpacc[p][r] + nd);
+          const float e = keep_bit(keep, 16 * ks + t, exp2_hw(fmaf(sacc[p][r], c2, nlc)));
+          d8[t] = e * (dpacc[p][r] + nd);
         }
-        sf[p][ks] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        sf[p][ks] = to_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
       }
-    }
+    };
 
     if constexpr (kN > 0) {
       bf16x8_t fq[kLook + 1];
@@ -688,37 +795,51 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int i = 0; i < kN; ++i) {
         if (i + kLook < kN) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook);
         product(i, fq[i % (kLook + 1)]);
+        if constexpr (kVV) {
+#pragma unroll
+          for (int q = i * 32 / kN; q < (i + 1) * 32 / kN; ++q) vpiece(q);
+        }
+        if constexpr (kDma) {
+#pragma unroll
+          for (int k = 0; k < kPieces; ++k)
+            if (k * kN / kPieces + kN / (2 * kPieces) == i) dma_piece(dt, k);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      pin_order<kN1, kN2, 0, kVV ? 2 : 0>(std::make_integer_sequence<int, kN>{});
+    }
+    if constexpr (kVV) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        sf[p][ks] = __builtin_bit_cast(bf16x8_t, u32x4_t{sw[4 * ks], sw[4 * ks + 1], sw[4 * ks + 2], sw[4 * ks + 3]});
+      if constexpr (kMask) {
+        if (block_masked(j)) probs_masked();
+      }
     }
   };
 
   if (nt > 0) {
-    issue(0);
-    if (nt > 1) issue(1);
-    if (nt > 1) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    constexpr Bool<true> y{};
+    constexpr Bool<false> n{};
+    {
+      const DmaTile t0 = dma_setup(0), t1 = dma_setup(1);
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) dma_piece(t0, k);
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) dma_piece(t1, k);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
     barrier();
-    if (nt > 2) issue(2);
-    step(Bool<true>{}, Bool<false>{}, Bool<false>{}, Bool<false>{}, Int<1>{}, -1);
-    step(Bool<true>{}, Bool<false>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 0);
-    // every block applies its element mask, as in the dK, dV kernel
+    step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
+    step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
     for (int u = 1; u < nt; ++u) {
-      if (u + 1 < nt) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
       barrier();
-      if (u + 2 < nt) issue(u + 2);
-      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * u - 1);
-      step(Bool<true>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<0>{}, 2 * u);
+      step(y, y, y, y, Int<1>{}, y, dma_setup(u + 2), 2 * u - 1);
+      step(y, y, y, y, Int<0>{}, n, DmaTile{}, 2 * u);
     }
-    step(Bool<false>{}, Bool<true>{}, Bool<true>{}, Bool<true>{}, Int<1>{}, 2 * nt - 1);
-    step(Bool<false>{}, Bool<true>{}, Bool<false>{}, Bool<false>{}, Int<0>{}, 2 * nt);
+    step(n, y, y, y, Int<1>{}, n, DmaTile{}, 2 * nt - 1);
+    step(n, y, n, n, Int<0>{}, n, DmaTile{}, 2 * nt);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
   if (row_live) {
