@@ -26,7 +26,10 @@ so that the engine clock has left its idle ramp before the warmup steps.
 ``--profile-target NAME`` runs only NAME's launches (plus, with
 ``--calibrate-copy``, a plain device copy of known size) for rocprofv3.
 ``--pmc-summary FETCH_DIR WRITE_DIR`` turns two ``rocprofv3 --pmc`` runs into
-the committed traffic summary under profiles/.
+the committed traffic summary under profiles/; ``--mfma-summary UTIL_DIR
+RAW_DIR`` does the same for the matrix-pipe utilisation counters, which the
+bench line reports as ``roofline.mfma_util_counters`` (per cent of GPU-active
+cycles the matrix pipes were busy) while the summary matches the kernel source.
 """
 
 from __future__ import annotations
@@ -53,6 +56,7 @@ PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_pre
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_mfma_util.txt")
 COPY_BYTES = 512 << 20
 
 
@@ -391,6 +395,76 @@ def pmc_summary(fetch_dir, write_dir, target, out_path, cmd):
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE")
+
+def _kernel_short(name):
+    return name.replace("void fa::(anonymous namespace)::", "").split("(fa::")[0]
+
+
+def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
+    """Matrix-pipe utilisation of every library kernel of one workload from two
+    rocprofv3 --pmc passes: the derived MfmaUtil (MFMA busy cycles over all
+    SIMDs / (GPU active cycles x SIMDs)), and raw counters, medians per
+    dispatch (GRBM_GUI_ACTIVE comes back summed over the XCDs)."""
+    util = {}
+    for r in _pmc_rows(util_dir):
+        if r.get("Counter_Name") == "MfmaUtil" and "fa::" in r.get("Kernel_Name", ""):
+            util.setdefault(_kernel_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    raw, dur = {}, {}
+    for r in _pmc_rows(raw_dir):
+        n = r.get("Kernel_Name", "")
+        if "fa::" not in n:
+            continue
+        k = _kernel_short(n)
+        raw.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+            dur.setdefault(k, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    lines = [f"# MFMA utilisation of the {target} workload's kernels from two rocprofv3 --pmc passes",
+             f"command: {cmd}",
+             f"algorithmic_flops_per_launch: {algo_flops}",
+             "(medians over the dispatches of each kernel; the settle launches before the timed"
+             " ones are included)"]
+    for k in sorted(util):
+        med = {c: statistics.median(v) for c, v in raw.get(k, {}).items()}
+        lines.append(f"kernel: {k}")
+        lines.append(f"  dispatches: {len(util[k])}")
+        lines.append(f"  mfma_util_pct: {statistics.median(util[k]):.2f}")
+        for c in MFMA_COUNTERS:
+            if c in med:
+                lines.append(f"  {c}: {med[c]:.0f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+            lines.append(f"  mfma_flops_bf16: {med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.0f}")
+        if k in dur:
+            lines.append(f"  dispatch_us_under_counters: {statistics.median(dur[k]) * 1e6:.2f}")
+    src = PREFILL_KERNEL_SRC
+    lines.append(f"kernel_source_sha256: {sha256(src)}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_mfma_util(summary, src, kernel):
+    """MfmaUtil (per cent) of one kernel from a committed counter summary, or
+    None when absent or taken on another version of the kernel source."""
+    if not os.path.exists(summary):
+        return None
+    util, cur, sha = {}, None, None
+    with open(summary) as f:
+        for line in f:
+            key, _, val = line.strip().partition(":")
+            if key == "kernel":
+                cur = val.strip()
+            elif key == "mfma_util_pct" and cur:
+                util[cur] = float(val)
+            elif key == "kernel_source_sha256":
+                sha = val.strip()
+    if sha != sha256(src):
+        return None
+    return util.get(kernel)
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -411,7 +485,14 @@ def main():
     ap.add_argument("--pmc-target", default="prefill_2k")
     ap.add_argument("--pmc-out", default=None)
     ap.add_argument("--pmc-cmd", default="")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("UTIL_DIR", "RAW_DIR"))
+    ap.add_argument("--algo-flops", type=int, default=0)
     args = ap.parse_args()
+
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary[0], args.mfma_summary[1], args.pmc_target, args.pmc_out,
+                     args.pmc_cmd, args.algo_flops)
+        return 0
 
     if args.pmc_summary:
         out = args.pmc_out or (TRAFFIC_SUMMARY if args.pmc_target.startswith("prefill")
@@ -496,6 +577,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "mfma_util_counters": read_mfma_util(MFMA_SUMMARY, PREFILL_KERNEL_SRC,
+                                                 "fwd_bf16_kernel<128, false>"),
             "kernel": "fwd_bf16_kernel<128,false>",
             "flops_per_launch": head.work,
             "mean_launch_ms": round(mean_ms, 5),
