@@ -45,7 +45,11 @@
 //    wave in its matrix block raises its issue priority.  Tiles stream
 //    through a ring of four LDS slots two tiles ahead of use; the loads are
 //    queued with inline assembly so that the only waits for them are the
-//    explicit ones before each step's barrier.
+//    explicit ones before each step's barrier.  Plain dense launches are
+//    persistent: one workgroup per CU walks several query tiles, and each
+//    tile's last landing barrier queues the next tile's first K/V tiles and
+//    Q fragments, so their latency runs under the last P V block and the
+//    output stores.
 // d = 64: four-wave kernel.  4 waves (128 query rows) per workgroup, two
 //    workgroups per CU, double-buffered tiles, one barrier per tile.  At
 //    d = 64 the softmax work per tile is as large as at d = 128 while the
@@ -91,7 +95,7 @@ struct Work {
   long long lse_base;     // lse offset of the sequence's row 0 for head h
 };
 
-__device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
+__device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w, int item, int n_items) {
   const int nbh = a.batch * a.heads;
   int bh, t;  // t: rank of the tile in start order, 0 = started first
   if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
@@ -102,11 +106,11 @@ __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w) {
     // longest first, so the short tiles fill in behind the long ones
     // (longest-processing-time order); each unit's tiles stay on one XCD and
     // share its L2.
-    const int x = blockIdx.x & 7, k = blockIdx.x >> 3, hx = nbh >> 3;
+    const int x = item & 7, k = item >> 3, hx = nbh >> 3;
     t = k / hx;
     bh = x + 8 * (k - t * hx);
   } else {
-    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int id = xcd_contiguous(item, n_items);
     bh = id / nqt;
     t = id - bh * nqt;
   }
@@ -334,41 +338,75 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int half = lane >> 5, l32 = lane & 31;
   const int lg = lane >> 4, j16 = lane & 15;
 
-  Work w;
-  if constexpr (VARLEN) {
-    if (!varlen_work(a, kBR, lane, w)) return;
-  } else {
-    dense_work(a, ceil_div(a.seqlen_q, kBR), w);
-  }
-
   const long long rs = (long long)a.heads * D;  // elements between consecutive rows
-  const uint16_t* qg = (const uint16_t*)a.q + (w.q_row0 * a.heads + w.h) * D;
-  const uint16_t* kg = (const uint16_t*)a.k + (w.k_row0 * a.heads + w.h) * D;
-  const uint16_t* vg = (const uint16_t*)a.v + (w.k_row0 * a.heads + w.h) * D;
-  uint16_t* og = (uint16_t*)a.o + (w.q_row0 * a.heads + w.h) * D;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
-
-  const int n_q = w.n_q, n_k = w.n_k, delta = n_k - n_q;
   const int causal = a.causal, W = a.window_left;
   const float c2 = a.scale_log2;
-  const int q0 = w.qt * kBR;
-  const int q_last = min(q0 + kBR, n_q) - 1;
 
-  // K/V tiles the workgroup needs (fully masked ones are skipped)
-  int kv_lo = 0, kv_hi = n_k;
-  if (causal) kv_hi = min(kv_hi, q_last + delta + 1);
-  if (W >= 0) kv_lo = max(kv_lo, q0 + delta - W);
-  const int t_lo = kv_lo / kBC;
-  const int nt = kv_hi > kv_lo ? ceil_div(kv_hi, kBC) - t_lo : 0;
+  // Work items (query tiles of one (sequence, head)).  Dense launches may be
+  // persistent: workgroup b takes items b, G + b', 2 G + b, ... (G = grid
+  // size, a multiple of 8 when there is more than one round, so every item
+  // of a workgroup belongs to its XCD); odd rounds take the mirror image b'
+  // of b within its XCD, which pairs long causal tiles with short ones.
+  // Varlen and single-round launches run one item per workgroup.
+  const int nqt = ceil_div(a.seqlen_q, kBR);
+  const int n_items = VARLEN ? (int)gridDim.x : a.batch * a.heads * nqt;
+  auto item_id = [&](int r) {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int bm = (r & 1) && (G & 7) == 0 ? (((G >> 3) - 1 - (b >> 3)) << 3) + (b & 7) : b;
+    return r * G + bm;
+  };
 
-  // this wave's rows and key range
-  const int wq0 = q0 + rblk * 32;
-  const bool wave_live = wq0 < n_q;
-  const int wq_last = min(wq0 + 31, n_q - 1);
-  int w_lo = 0, w_hi = n_k;
-  if (causal) w_hi = min(w_hi, wq_last + delta + 1);
-  if (W >= 0) w_lo = max(w_lo, wq0 + delta - W);
-  const int qi = wq0 + l32;  // this lane's query row
+  // per-item state
+  struct Item {
+    const uint16_t* qg;
+    const uint16_t* kg;
+    const uint16_t* vg;
+    uint16_t* og;
+    long long lse_base;
+    int n_q, n_k, t_lo, nt, wq0, wq_last, w_lo, w_hi;
+    bool wave_live;
+    int seg0, seg_end;
+    u32x4_t rk, rv;
+  };
+  auto make_item = [&](int id, Item& it) -> bool {
+    Work w;
+    if constexpr (VARLEN) {
+      if (!varlen_work(a, kBR, lane, w)) return false;
+    } else {
+      if (id >= n_items) return false;
+      dense_work(a, nqt, w, id, n_items);
+    }
+    it.qg = (const uint16_t*)a.q + (w.q_row0 * a.heads + w.h) * D;
+    it.kg = (const uint16_t*)a.k + (w.k_row0 * a.heads + w.h) * D;
+    it.vg = (const uint16_t*)a.v + (w.k_row0 * a.heads + w.h) * D;
+    it.og = (uint16_t*)a.o + (w.q_row0 * a.heads + w.h) * D;
+    it.lse_base = w.lse_base;
+    it.n_q = w.n_q;
+    it.n_k = w.n_k;
+    const int delta = w.n_k - w.n_q;
+    const int q0 = w.qt * kBR;
+    const int q_last = min(q0 + kBR, w.n_q) - 1;
+    // K/V tiles the workgroup needs (fully masked ones are skipped)
+    int kv_lo = 0, kv_hi = w.n_k;
+    if (causal) kv_hi = min(kv_hi, q_last + delta + 1);
+    if (W >= 0) kv_lo = max(kv_lo, q0 + delta - W);
+    it.t_lo = kv_lo / kBC;
+    it.nt = kv_hi > kv_lo ? ceil_div(kv_hi, kBC) - it.t_lo : 0;
+    // this wave's rows and key range
+    it.wq0 = q0 + rblk * 32;
+    it.wave_live = it.wq0 < w.n_q;
+    it.wq_last = min(it.wq0 + 31, w.n_q - 1);
+    it.w_lo = 0;
+    it.w_hi = w.n_k;
+    if (causal) it.w_hi = min(it.w_hi, it.wq_last + delta + 1);
+    if (W >= 0) it.w_lo = max(it.w_lo, it.wq0 + delta - W);
+    it.seg0 = 0;
+    it.seg_end = -1;
+    it.rk = buffer_rsrc(it.kg, 0);
+    it.rv = buffer_rsrc(it.vg, 0);
+    return true;
+  };
 
   // K/V streaming: one buffer descriptor per tensor covers a window of
   // seg_rows key rows from seg0 (32-bit offsets); rows past the sequence end
@@ -384,50 +422,75 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
     kofs[i] = (uint32_t)r * row_bytes + (uint32_t)ck * 16;
     vofs[i] = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
   }
-  int seg0 = 0, seg_end = -1;
-  u32x4_t rk = buffer_rsrc(kg, 0), rv = buffer_rsrc(vg, 0);
-  // queue the DMA of tile j (relative to t_lo) into the given slot
-  auto issue = [&](int j, char* kdst, char* vdst) {
-    const int k0 = (t_lo + j) * kBC;
-    if (k0 + kBC > seg_end) {
-      seg0 = k0;
-      seg_end = k0 + a.seg_rows;
-      const uint32_t nrec = (uint32_t)min(n_k - k0, a.seg_rows) * row_bytes;
-      rk = buffer_rsrc(kg + (long long)k0 * rs, nrec);
-      rv = buffer_rsrc(vg + (long long)k0 * rs, nrec);
+  // ring slot of tile g, counted over all items of the workgroup
+  auto kslot = [&](int g) { return ring + (g & 3) * 2 * T::kBytes; };
+  auto vslot = [&](int g) { return ring + (g & 3) * 2 * T::kBytes + T::kBytes; };
+  // queue the DMA of tile j (relative to the item's t_lo) into slot g
+  auto issue = [&](Item& it, int j, int g) {
+    const int k0 = (it.t_lo + j) * kBC;
+    if (k0 + kBC > it.seg_end) {
+      it.seg0 = k0;
+      it.seg_end = k0 + a.seg_rows;
+      const uint32_t nrec = (uint32_t)min(it.n_k - k0, a.seg_rows) * row_bytes;
+      it.rk = buffer_rsrc(it.kg + (long long)k0 * rs, nrec);
+      it.rv = buffer_rsrc(it.vg + (long long)k0 * rs, nrec);
     }
-    const uint32_t base = (uint32_t)(k0 - seg0) * row_bytes;
+    const uint32_t base = (uint32_t)(k0 - it.seg0) * row_bytes;
+    char* kdst = kslot(g);
+    char* vdst = vslot(g);
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int blk = i * kWaves + wave;
-      dma16(rk, base + kofs[i], lds_addr(kdst + blk * 1024));
-      dma16(rv, base + vofs[i], lds_addr(vdst + blk * 1024));
+      dma16(it.rk, base + kofs[i], lds_addr(kdst + blk * 1024));
+      dma16(it.rv, base + vofs[i], lds_addr(vdst + blk * 1024));
     }
   };
-
-  auto kslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes; };
-  auto vslot = [&](int j) { return ring + (j & 3) * 2 * T::kBytes + T::kBytes; };
-  if (nt > 0) {
-    issue(0, kslot(0), vslot(0));
-    if (nt > 1) issue(1, kslot(1), vslot(1));
-  }
-
   // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
   // the sequence read as zeros through the descriptor bound
   bf16x8_t qf[D / 16];
-  {
-    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
+  auto load_q = [&](const Item& it) {
+    const uint32_t nrec =
+        __builtin_amdgcn_readfirstlane((uint32_t)max(min(it.n_q - it.wq0, 32), 0) * row_bytes);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
+        (void*)(it.qg + (long long)it.wq0 * rs), 0, nrec, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
           rq, (uint32_t)l32 * row_bytes + (uint32_t)(kk * 16 + half * 8) * 2, 0, 0);
       qf[kk] = __builtin_bit_cast(bf16x8_t, x);
     }
-    // Q and the first two tiles are in flight together; the wait covers all
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  // first two tiles and the Q fragments of an item, tiles into slots g, g + 1
+  auto start_loads = [&](Item& it, int g) {
+    if (it.nt > 0) {
+      issue(it, 0, g);
+      if (it.nt > 1) issue(it, 1, g + 1);
+    }
+    load_q(it);
+  };
+
+  int r_item = 0;
+  {
+    Item first;
+    if (!make_item(item_id(0), first)) return;
+    start_loads(first, 0);
   }
+  int gbase = 0;  // ring index of the current item's tile 0
+
+  for (;;) {
+  // the item's state is derived again here (its loads were queued earlier;
+  // the K/V descriptor window restarts at the first tile queued from here)
+  Item cur;
+  make_item(item_id(r_item), cur);
+  uint16_t* const og = cur.og;
+  const int n_q = cur.n_q, n_k = cur.n_k, delta = n_k - n_q;
+  const int t_lo = cur.t_lo, nt = cur.nt;
+  const int wq0 = cur.wq0, wq_last = cur.wq_last, w_lo = cur.w_lo, w_hi = cur.w_hi;
+  const bool wave_live = cur.wave_live;
+  const int qi = wq0 + l32;  // this lane's query row
+  // Q and the first two tiles are in flight together (with the previous
+  // item's output stores); the wait covers all
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   f32x16_t oacc[D / 32];
 #pragma unroll
@@ -641,44 +704,59 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   // the slot of tile j - 2 is free once step j has landed; the loads are
   // queued at the end of a vector block, where the wave would otherwise wait
   auto prefetch = [&](int j) {
-    if (j + 2 < nt) issue(j + 2, kslot(j + 2), vslot(j + 2));
+    if (j + 2 < nt) issue(cur, j + 2, gbase + j + 2);
+  };
+  // the next item's first tiles and Q fragments: queued once this item's
+  // last tile has landed everywhere (its slots gbase + nt, gbase + nt + 1
+  // held tiles nt - 4 and nt - 3, which every wave has finished) and the
+  // score products no longer read Q
+  const bool has_next = !VARLEN && item_id(r_item + 1) < n_items;
+  auto next_loads = [&]() {
+    if constexpr (!VARLEN) {
+      Item nxt;
+      if (has_next && make_item(item_id(r_item + 1), nxt)) start_loads(nxt, gbase + nt);
+    }
   };
 
   if (nt > 0) {
     // steps 0 .. nt: step 0 has no previous tile, step nt no next one
     if (group == 0) {
       land(0);
-      mblock_first(kslot(0));
+      mblock_first(kslot(gbase));
       barrier();
       vblock(0);
       prefetch(0);
       for (int j = 1; j < nt; ++j) {
         land(j);
-        mblock(kslot(j), vslot(j - 1));
+        mblock(kslot(gbase + j), vslot(gbase + j - 1));
         barrier();
         vblock(j);
         prefetch(j);
       }
       land(nt);
-      mblock_last(vslot(nt - 1));
+      next_loads();
+      mblock_last(vslot(gbase + nt - 1));
       barrier();  // pairs with group 1's barrier before its last matrix block
     } else {
       land(0);
       prefetch(0);
       barrier();
-      mblock_first(kslot(0));
+      mblock_first(kslot(gbase));
       for (int j = 1; j < nt; ++j) {
         land(j);
         vblock(j - 1);
         prefetch(j);
         barrier();
-        mblock(kslot(j), vslot(j - 1));
+        mblock(kslot(gbase + j), vslot(gbase + j - 1));
       }
       land(nt);
+      next_loads();
       vblock(nt - 1);
       barrier();
-      mblock_last(vslot(nt - 1));
+      mblock_last(vslot(gbase + nt - 1));
     }
+  } else {
+    next_loads();
   }
 
   // epilogue: O = u / l (one division per row, l over the rounded
@@ -699,7 +777,11 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
         *(u32x2_t*)(op + d) = pr;
       }
     if (a.lse != nullptr && half == 0)
-      a.lse[w.lse_base + qi] = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : kNegInf;
+      a.lse[cur.lse_base + qi] = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : kNegInf;
+  }
+  if (!has_next) break;
+  gbase += nt;
+  ++r_item;
   }
 }
 
@@ -758,7 +840,7 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
   if constexpr (VARLEN) {
     if (!varlen_work(a, kQRows, lane, w)) return;
   } else {
-    dense_work(a, ceil_div(a.seqlen_q, kQRows), w);
+    dense_work(a, ceil_div(a.seqlen_q, kQRows), w, blockIdx.x, gridDim.x);
   }
 
   const long long rs = (long long)a.heads * D;  // elements between consecutive rows
@@ -980,7 +1062,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fwd_fp32_kernel(FwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
 
   Work w;
-  dense_work(a, ceil_div(a.seqlen_q, kBR32), w);
+  dense_work(a, ceil_div(a.seqlen_q, kBR32), w, blockIdx.x, gridDim.x);
   const long long rs = (long long)a.heads * D;
   const float* qg = (const float*)a.q + (w.q_row0 * a.heads + w.h) * D;
   const float* kg = (const float*)a.k + (w.k_row0 * a.heads + w.h) * D;
@@ -1109,12 +1191,28 @@ __global__ __launch_bounds__(kThreads32, 2) void fwd_fp32_kernel(FwdArgs a) {
   }
 }
 
+// Compute units of the current device, rounded down to a multiple of 8 (one
+// persistent workgroup per CU; 0 if the query fails).
+static int persistent_slots() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n & ~7;
+}
+
 template <bool VARLEN>
 hipError_t launch_bf16_d128(const FwdArgs& a, hipStream_t stream) {
   const int nqt = ceil_div(a.seqlen_q, kBR);
-  const long long grid = (long long)a.batch * a.heads * nqt;
+  long long grid = (long long)a.batch * a.heads * nqt;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  // plain dense launches: one workgroup per CU walks the items (KV-cache
+  // launches keep one item per workgroup: their items differ in length in
+  // ways a static assignment cannot balance)
+  if (!VARLEN && a.seqlens_k == nullptr) {
+    const int slots = persistent_slots();
+    if (slots >= 8 && grid > slots) grid = slots;
+  }
   hipLaunchKernelGGL((fwd_bf16_kernel<128, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();

@@ -106,6 +106,18 @@ def test_no_keys_at_all():
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("B,H,nq,nk,causal,W", [
+    (2, 64, 700, 400, True, -1),    # 384 items, partial second round; whole tiles without keys
+    (1, 264, 300, 300, False, -1),  # 528 items, partial third round, no mask
+    (2, 72, 520, 520, True, 200),   # 432 items, causal + window (first needed tile > 0)
+])
+def test_persistent_grid(B, H, nq, nk, causal, W):
+    """More d = 128 query tiles than compute units: each workgroup walks
+    several items (mirrored order in odd rounds, the next item's tiles and Q
+    queued during the current item's last step)."""
+    _dense_case(B, H, nq, nk, 128, causal, W, torch.bfloat16, seed=31)
+
+
 @pytest.mark.parametrize("B,H,nq,nk,d,causal,W", [
     (1, 2, 300, 300, 128, True, -1),
     (1, 1, 100, 37, 64, True, 5),
