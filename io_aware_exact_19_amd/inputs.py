@@ -10,6 +10,11 @@ synthetic):
 * "peaked" runs multiply the rounded Q by 4 (a power of two, so exact);
 * sequence lengths are integers drawn uniformly from [lo, hi] inclusive with
   ``torch.randint`` from their own sub-seed;
+* e4m3 workloads draw the same fp32 N(0, 1) values, pick one factor per
+  (batch, head) block of a tensor, amax / 448 (448 is the largest finite e4m3
+  value), and store round-to-nearest-even e4m3 codes of value / factor
+  (torch's float8_e4m3fn conversion); the factor is the block's
+  dequantisation factor;
 * KV caches too large for host memory are generated on the device, one
   sub-seed per sequence, and rows past each sequence's length are filled with
   NaN so that a read of padding shows up in the output.
@@ -78,3 +83,22 @@ def decode_cache(batch, max_len, heads, d, seqlens, seed, device, name, dtype=to
         if n < max_len:
             cache[b, n:] = pad
     return cache
+
+
+def fp8_tensor(shape, seed: int, mult: float = 1.0):
+    """e4m3 codes (uint8 [B, n, H, d]) and per-(batch, head) dequantisation
+    factors (float32 [B * H]) of i.i.d. N(0,1) values times ``mult``."""
+    x = normal(shape, seed, torch.float32) * mult
+    B, _, H, _ = x.shape
+    amax = x.abs().amax(dim=(1, 3))  # [B, H]
+    ds = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (x / ds[:, None, :, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), ds.reshape(-1).contiguous()
+
+
+def fp8_qkv(B, n_q, n_k, H, d, seed, q_mult: float = 1.0):
+    """(q8, k8, v8, descale_q, descale_k, descale_v) on the CPU."""
+    q8, dq = fp8_tensor((B, n_q, H, d), subseed(seed, "q"), q_mult)
+    k8, dk = fp8_tensor((B, n_k, H, d), subseed(seed, "k"))
+    v8, dv = fp8_tensor((B, n_k, H, d), subseed(seed, "v"))
+    return q8, k8, v8, dq, dk, dv

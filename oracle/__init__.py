@@ -10,8 +10,10 @@ from .attention import (  # noqa: F401
     attention_backward,
     attention_dense,
     attention_flops,
+    attention_fp8,
     attention_kvcache,
     attention_varlen,
+    e4m3_decode,
     merge_states,
     online_attention,
     sdpa,

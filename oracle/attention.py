@@ -37,13 +37,22 @@ What it computes, and where the pages fix it:
   applied to whole chunk states (a chunk state (m_c, l_c, u_c) has
   o_c = u_c / l_c and lse_c = m_c + ln l_c).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * causal alignment is bottom-right: key j is allowed for query i iff
   j <= i + (n_k - n_q);
 * a left window of W keys admits keys j >= i + (n_k - n_q) - W, so with the
   causal bound a row sees at most W + 1 keys; W < 0 means no window;
 * a row with no allowed key outputs zeros and lse = -inf.
+
+* ``attention_fp8`` is the same attention on 8-bit floating-point inputs,
+  the low-precision variant named in "FlashAttention", section "Versions":
+  each e4m3 code is decoded to its exact value (``e4m3_decode``, written from
+  the OCP float8 e4m3 definition: sign, 4 exponent bits with bias 7, 3
+  mantissa bits, exponent field 0 subnormal, S.1111.111 NaN, no infinities),
+  multiplied by the dequantisation factor of its (batch, head) block, and the
+  fp64 definition above runs on the result.  The GPU path's own rounding of
+  the probabilities is not part of the definition.
 
 All functions take numpy arrays of any float dtype and compute in fp64.
 """
@@ -64,6 +73,8 @@ __all__ = [
     "online_attention",
     "merge_states",
     "attention_flops",
+    "e4m3_decode",
+    "attention_fp8",
 ]
 
 
@@ -345,3 +356,37 @@ def attention_flops(n_q, n_k, d, causal=False, window_left=-1):
         if hi >= lo:
             pairs += hi - lo + 1
     return 4 * d * pairs
+
+
+def e4m3_decode(codes):
+    """Exact fp64 values of OCP e4m3 codes (uint8 array of any shape).
+
+    Bit layout s eeee mmm: exponent field e > 0 gives (-1)^s (1 + m/8) 2^(e-7),
+    e = 0 gives the subnormals (-1)^s (m/8) 2^-6, and the two codes with
+    e = 15 and m = 7 are NaN (the format has no infinities; 0xFE = -448 is
+    the most negative finite value).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = c >> 7
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(sign == 1, -mag, mag)
+
+
+def attention_fp8(q8, k8, v8, descale_q, descale_k, descale_v, scale, causal=False,
+                  window_left=-1):
+    """Dense attention on e4m3 codes q8 [B, n_q, H, d], k8/v8 [B, n_k, H, d]
+    with one dequantisation factor per (batch, head) and tensor (arrays of
+    B * H values, batch-major).  Returns o [B, n_q, H, d] and lse [B, H, n_q],
+    fp64, of ``attention_dense`` on the dequantised tensors."""
+    q8 = np.asarray(q8)
+    B, _, H, _ = q8.shape
+
+    def deq(codes, ds):
+        f = np.asarray(ds, dtype=np.float64).reshape(B, 1, H, 1)
+        return e4m3_decode(codes) * f
+
+    return attention_dense(deq(q8, descale_q), deq(k8, descale_k), deq(v8, descale_v), scale,
+                           causal, window_left)
