@@ -17,7 +17,8 @@ timed steps.  The line also carries:
 * ``secondary``: the other workloads (causal 2k, 8000-token causal prompt,
   packed varlen with a 1024-key window, fp32 small case, KV-cache decode in
   HBM GB/s, chunked prefill of 512 new tokens against KV caches, and the
-  backward pass of the headline shape, plain and causal), each timed the same
+  backward pass of the headline shape, plain and causal, and the headline
+  shape on e4m3 inputs against the fp8 matrix-core peak), each timed the same
   way.
 
 Every workload first runs back to back for ``--settle-ms`` (default 400 ms)
@@ -51,6 +52,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (bf16) and % MFMA peak; decode KV-read HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix-core peak
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
@@ -224,6 +226,34 @@ def make_backward(torch, fa, inputs, configs, cfg, causal=False):
     w = Workload(name, launch, 10 * d * H * B * pairs, "TFLOP/s", PEAK_BF16_TFLOPS, "mfma", "bf16",
                  conf)
     w.tensors = (q, k, v, do, o, lse)
+    return w
+
+
+def make_fp8(torch, fa, inputs, configs, cfg, causal=False):
+    """The headline shape on e4m3 inputs with per-(batch, head) factors; one
+    call = the V transpose into the workspace plus the forward kernel."""
+    B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
+    q8, k8, v8, dq, dk, dv = (x.cuda() for x in inputs.fp8_qkv(B, N, N, H, d, cfg["seed"]))
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    need = fa.fa_fwd_fp8_workspace_size(B, H, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    s = configs.default_scale(d)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        st = fa.fa_fwd_fp8(q8, k8, v8, o, lse, dq, dk, dv, B, H, N, N, d, s, int(causal), -1, ws,
+                           need, stream)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_fp8")
+
+    pairs = N * (N + 1) // 2 if causal else N * N
+    name = f"fp8_e4m3_b{B}_h{H}_n{N}_d{d}" + ("_causal" if causal else "")
+    conf = dict(workload=name, batch=B, heads=H, seqlen=N, d=d, causal=causal,
+                inputs="e4m3 codes, one factor per (batch, head)", output="bf16")
+    w = Workload(name, launch, 4 * d * H * B * pairs, "TFLOP/s", PEAK_FP8_TFLOPS, "mfma",
+                 "fp8-e4m3", conf)
+    w.tensors = (q8, k8, v8, dq, dk, dv, ws)
     return w
 
 
@@ -479,7 +509,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-target", default=None,
                     choices=["prefill_2k", "prefill_2k_causal", "long_8k", "varlen", "small_fp32",
-                             "decode", "kvcache", "backward", "backward_causal"])
+                             "decode", "kvcache", "backward", "backward_causal", "fp8",
+                             "fp8_causal"])
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-target", default="prefill_2k")
@@ -532,6 +563,8 @@ def main():
         "backward": lambda: make_backward(torch, fa, inputs, configs, configs.PREFILL_2K),
         "backward_causal": lambda: make_backward(torch, fa, inputs, configs, configs.PREFILL_2K,
                                                  causal=True),
+        "fp8": lambda: make_fp8(torch, fa, inputs, configs, configs.PREFILL_2K),
+        "fp8_causal": lambda: make_fp8(torch, fa, inputs, configs, configs.PREFILL_2K, causal=True),
     }
 
     if args.profile_target:
@@ -592,7 +625,7 @@ def main():
     if not args.no_secondary:
         sec = []
         for key in ("prefill_2k_causal", "long_8k", "varlen", "small_fp32", "decode", "kvcache",
-                    "backward", "backward_causal"):
+                    "backward", "backward_causal", "fp8", "fp8_causal"):
             w = builders[key]()
             steps = 20 if key != "decode" else 10
             log(f"[bench] timing {w.name}")

@@ -54,7 +54,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, scale not finite > 0 */
   FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: head dim, chunk size, varlen+fp32,
                               a grid over 2^31 workgroups, a key row (heads*d) over 64 MiB */
-  FA_ERR_WORKSPACE = -3,   /* decode workspace missing or smaller than required */
+  FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
 } fa_status;
 
@@ -173,6 +173,41 @@ size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int ch
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
               void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
               int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_fp8_workspace_size -- bytes of device workspace fa_fwd_fp8 needs:
+ * the transposed V, batch * heads * d * ceil(seqlen_k / 64) * 64 bytes.
+ * 0 when any size is <= 0 or d != 128.
+ */
+size_t fa_fwd_fp8_workspace_size(int batch, int heads, int seqlen_k, int d);
+
+/*
+ * fa_fwd_fp8 -- attention forward (dense) on 8-bit floating-point inputs, the
+ * low-precision variant named in "FlashAttention" (aiwiki.page), section
+ * "Versions".  q, k, v hold OCP e4m3 codes (1 byte each, the float8_e4m3fn
+ * format: sign, 4 exponent bits with bias 7, 3 mantissa bits, 0x7F/0xFF NaN,
+ * no infinities) in the layouts of fa_fwd's dense mode; each (batch, head)
+ * block of a tensor carries one dequantisation factor:
+ *     Q = descale_q[b * heads + h] * decode(q), likewise K and V.
+ * descale_*: device fp32 [batch * heads], 4-byte aligned.  The call computes
+ * the attention of fa_fwd (same scale, causal and window_left semantics) on
+ * the dequantised tensors and writes o as bf16 [batch, seqlen_q, heads, d]
+ * and lse as fp32 [batch, heads, seqlen_q] (lse may be NULL).
+ * Arithmetic: Q K^T and P V on the fp8 matrix instructions with fp32
+ * accumulation, the softmax in fp32, the probabilities rounded to e4m3 before
+ * the P V product, O divided by the sum of exactly those rounded
+ * probabilities (so each output row is a convex combination of V rows),
+ * lse from the unrounded sum.
+ * workspace: device, 16-byte aligned, >= fa_fwd_fp8_workspace_size(); it
+ * receives V transposed to [batch, heads, d, keys] (contents on return are
+ * unspecified; may be NULL when seqlen_k == 0).  FA_ERR_UNSUPPORTED for
+ * d != 128, more than 65535 (batch, head) pairs, or key rows and transposed
+ * blocks past 32-bit offsets.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const float* descale_q, const float* descale_k, const float* descale_v, int batch,
+               int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
+               int window_left, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

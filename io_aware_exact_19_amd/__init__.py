@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     FAError,
     attention,
     attention_backward,
+    attention_fp8,
     attention_kvcache,
     attention_varlen,
     decode,
@@ -23,6 +24,8 @@ from .binding import (  # noqa: F401
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_fp32,
+    fa_fwd_fp8,
+    fa_fwd_fp8_workspace_size,
     fa_fwd_kvcache,
     fa_status_string,
     load_library,

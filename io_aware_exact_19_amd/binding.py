@@ -7,7 +7,7 @@ same arguments as in ``include/fa.h``; pointer arguments may be torch tensors
 ``torch.cuda.Stream``, a raw handle or None (torch's current stream).  They
 return the C status code.
 
-``attention``, ``attention_varlen`` and ``decode`` are conveniences on top:
+``attention``, ``attention_varlen``, ``attention_fp8`` and ``decode`` are conveniences on top:
 they check tensor shapes, allocate the outputs with torch (device memory is
 all torch provides here) and raise ``FAError`` on a non-zero status.  Every
 arithmetic step runs in the library's kernels; there is no other path.
@@ -30,7 +30,8 @@ FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_decode_workspace_size", "fa_decode", "fa_status_string")
+            "fa_decode_workspace_size", "fa_decode", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8",
+            "fa_status_string")
 
 _lib = None
 
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_size.restype = Z
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode.restype = I
+    lib.fa_fwd_fp8_workspace_size.argtypes = [I, I, I, I]
+    lib.fa_fwd_fp8_workspace_size.restype = Z
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P]
+    lib.fa_fwd_fp8.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -135,6 +140,18 @@ def fa_decode(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d, 
     return load_library().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k),
                                     _ptr(o), _ptr(lse), batch, heads, max_len, d, scale, chunk,
                                     _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d) -> int:
+    return int(load_library().fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, batch, heads, seqlen_q, seqlen_k,
+               d, scale, causal, window_left, workspace, workspace_bytes, stream=None) -> int:
+    return load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), batch,
+                                     heads, seqlen_q, seqlen_k, d, scale, int(causal), window_left,
+                                     _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def fa_status_string(status: int) -> str:
@@ -287,4 +304,37 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale=None, chunk=256, workspace=N
                    workspace, workspace.numel() * workspace.element_size(), stream)
     if st != FA_OK:
         raise FAError(st, "fa_decode")
+    return o, lse
+
+
+def attention_fp8(q, k, v, descale_q, descale_k, descale_v, *, scale=None, causal=False,
+                  window_left=-1, return_lse=True, workspace=None, stream=None):
+    """Dense attention on e4m3 codes: q [B, n_q, H, 128], k/v [B, n_k, H, 128]
+    torch.uint8 (or torch.float8_e4m3fn) on the GPU, descale_* fp32 [B * H]
+    (or [B, H]).  Returns (o [B, n_q, H, 128] bf16, lse [B, H, n_q] fp32 or None)."""
+    q, k, v = (t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q, k, v))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, torch.uint8, 4)
+    B, n_q, H, d = q.shape
+    if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    n_k = k.shape[1]
+    ds = []
+    for name, t in (("descale_q", descale_q), ("descale_k", descale_k), ("descale_v", descale_v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a float32 tensor on the GPU")
+        if t.numel() != B * H or not t.is_contiguous():
+            raise ValueError(f"{name} must hold batch * heads contiguous values")
+        ds.append(t)
+    o = torch.empty((B, n_q, H, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if return_lse else None
+    need = fa_fwd_fp8_workspace_size(B, H, n_k, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = fa_fwd_fp8(q, k, v, o, lse, ds[0], ds[1], ds[2], B, H, n_q, n_k, d, s, int(causal),
+                    int(window_left), workspace, workspace.numel() * workspace.element_size(),
+                    stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
     return o, lse

@@ -7,13 +7,15 @@ The library lands next to this file so that it travels with the source tree.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_backward.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_backward.hip", "fa_fp8.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,6 +37,40 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+_MFMA8 = re.compile(r"v_mfma_scale_f32_32x32x64_f8f6f4 v\[(\d+):(\d+)\], v\[(\d+):(\d+)\], "
+                    r"v\[(\d+):(\d+)\]")
+
+
+def check_fp8_operand_overlap(extra_flags=None) -> int:
+    """Compile the fp8 kernels to assembly and fail if the result registers of
+    any fp8 matrix instruction overlap its operand registers: this compiler
+    allows such an allocation when the accumulator input is not tied to the
+    result, and the instruction then reads back garbage.  Returns the number
+    of instructions checked."""
+    src = os.path.join(CSRC, "fa_fp8.hip")
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "fa_fp8.s")
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *(extra_flags or []),
+               "-o", out, src]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc -S failed with exit code {res.returncode}")
+        n = 0
+        for line in open(out):
+            m = _MFMA8.search(line)
+            if not m:
+                continue
+            n += 1
+            d0, d1, a0, a1, b0, b1 = (int(x) for x in m.groups())
+            if not (d1 < a0 or a1 < d0) or not (d1 < b0 or b1 < d0):
+                raise RuntimeError(f"fp8 matrix instruction with overlapping registers: {line.strip()}")
+    if n == 0:
+        raise RuntimeError("no fp8 matrix instruction found in fa_fp8.hip's assembly")
+    return n
+
+
 def build_library(verbose: bool = False, extra_flags=None) -> str:
     """Compile every HIP source into libfa.so; returns the library path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
@@ -48,6 +84,9 @@ def build_library(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
     if verbose and res.stderr.strip():
         sys.stderr.write(res.stderr)
+    n = check_fp8_operand_overlap(extra_flags)
+    if verbose:
+        print(f"fp8 matrix instructions checked for register overlap: {n}", flush=True)
     os.replace(tmp, LIB)
     return LIB
 

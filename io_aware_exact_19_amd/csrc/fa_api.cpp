@@ -202,12 +202,68 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_fwd_fp8_workspace_size(int batch, int heads, int seqlen_k, int d) {
+  if (batch <= 0 || heads <= 0 || seqlen_k <= 0 || d != 128) return 0;
+  return fa::fp8_workspace_bytes(batch, heads, seqlen_k, d);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               const float* descale_q, const float* descale_k, const float* descale_v, int batch,
+               int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
+               int window_left, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || descale_q == nullptr || descale_k == nullptr ||
+      descale_v == nullptr)
+    return FA_ERR_INVALID_ARG;
+  if (seqlen_k > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4))
+    return FA_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return FA_ERR_WORKSPACE;
+  // 32-bit offsets: 64 key rows of K, 32 query rows, and one head's
+  // transposed V block (d x padded keys) must each stay below 4 GiB
+  const unsigned long long row_bytes = (unsigned long long)heads * d;
+  const unsigned long long n_kpad = ((unsigned long long)seqlen_k + 63) / 64 * 64;
+  if (row_bytes * 64 >= 0x100000000ull || n_kpad * d >= 0x100000000ull) return FA_ERR_UNSUPPORTED;
+  const long long grid = (long long)batch * heads * ((seqlen_q + 127) / 128);
+  if (grid > 0x7fffffffLL || (long long)batch * heads * (long long)(n_kpad / 64) > 0x7fffffffLL ||
+      (long long)batch * heads > 65535)
+    return FA_ERR_UNSUPPORTED;
+
+  fa::Fp8LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.descale_q = descale_q;
+  a.descale_k = descale_k;
+  a.descale_v = descale_v;
+  a.batch = batch;
+  a.heads = heads;
+  a.seqlen_q = seqlen_q;
+  a.seqlen_k = seqlen_k;
+  a.scale = scale;
+  a.causal = causal;
+  a.window_left = window_left;
+  a.workspace = workspace;
+  const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: combination not built";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: decode workspace missing or too small";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     default: return "unknown fa_status";
   }

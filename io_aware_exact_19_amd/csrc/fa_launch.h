@@ -77,4 +77,22 @@ struct BwdArgs {
 
 hipError_t launch_bwd(const BwdArgs& a, int d, hipStream_t stream);
 
+struct Fp8LaunchArgs {
+  const void* q;             // [batch, seqlen_q, heads, 128] e4m3
+  const void* k;             // [batch, seqlen_k, heads, 128] e4m3
+  const void* v;             // [batch, seqlen_k, heads, 128] e4m3
+  void* o;                   // [batch, seqlen_q, heads, 128] bf16
+  float* lse;                // [batch, heads, seqlen_q] or null
+  const float* descale_q;    // [batch * heads]
+  const float* descale_k;
+  const float* descale_v;
+  int batch, heads, seqlen_q, seqlen_k;
+  float scale;
+  int causal, window_left;
+  void* workspace;           // >= fp8_workspace_bytes(...): transposed V
+};
+
+size_t fp8_workspace_bytes(int batch, int heads, int seqlen_k, int d);
+hipError_t launch_fwd_fp8(const Fp8LaunchArgs& p, hipStream_t stream);
+
 }  // namespace fa

@@ -213,3 +213,50 @@ def test_binding_fails_loudly_without_library(tmp_path):
             b.load_library(str(tmp_path / "nope.so"))
     finally:
         b._lib = saved
+
+
+def _fp8(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, descale_q=P, descale_k=P, descale_v=P, batch=2,
+                heads=4, seqlen_q=64, seqlen_k=100, d=128, scale=0.125, causal=0, window_left=-1,
+                workspace=P, workspace_bytes=1 << 30, stream=NULL_STREAM)
+    args.update(kw)
+    return fa.fa_fwd_fp8(**args)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(descale_v=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=P + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=P + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(batch=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlen_k=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(workspace=0), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=P + 4), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_bytes=2 * 4 * 128 * 128 - 1), fa.FA_ERR_WORKSPACE),
+    (dict(batch=300, heads=300, workspace_bytes=1 << 40), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_fp8_rejects(lib, bad, code):
+    assert _fp8(**bad) == code
+
+
+def test_fwd_fp8_workspace_size(lib):
+    # V transposed to [batch, heads, d, keys rounded up to 64]
+    assert fa.fa_fwd_fp8_workspace_size(2, 4, 100, 128) == 2 * 4 * 128 * 128
+    assert fa.fa_fwd_fp8_workspace_size(1, 1, 64, 128) == 128 * 64
+    assert fa.fa_fwd_fp8_workspace_size(1, 1, 0, 128) == 0
+    assert fa.fa_fwd_fp8_workspace_size(1, 1, 64, 64) == 0
+
+
+@pytest.mark.parametrize("empty", [dict(batch=0), dict(heads=0), dict(seqlen_q=0)])
+def test_fwd_fp8_empty_is_noop(lib, empty):
+    assert _fp8(q=0, k=0, v=0, o=0, descale_q=0, descale_k=0, descale_v=0, **empty) == fa.FA_OK

@@ -1,0 +1,111 @@
+"""GPU parity of the fp8 (e4m3) forward against the fp64 oracle on the same
+dequantised inputs, element by element.
+
+Tolerance (the arithmetic fixes it; the pages give none for fp8): the
+kernel rounds every probability to e4m3 before the P V product, a relative
+error of at most 2^-4 per probability (3 mantissa bits, round to nearest
+even; smaller probabilities fall into e4m3's subnormals with absolute error
+at most 2^-10 on the kernel's scale, where the largest probability of a row
+is at least 1), and divides by the sum of exactly those rounded
+probabilities, so each output row stays a convex combination of V rows and
+the error of an element is sum_j w_j e_j (v_j - o) with e_j the relative
+roundings and w_j the weights.  With random roundings (standard deviation
+about 2^-4 / sqrt(3)) a flat row of n keys errs by about 0.036 / sqrt(n) of
+|v - o|, a row dominated by two or three keys by up to 0.036 of it, and the
+largest over millions of elements lies several standard deviations out.
+Bounds: max-abs <= FP8_MAX_ABS, mean-abs <= FP8_MEAN_ABS on bf16 outputs;
+lse (from the unrounded fp32 sum and exact fp8 products) within 1e-3; rows
+without an allowed key exactly O = 0, lse = -inf.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import io_aware_exact_19_amd as fa
+import oracle
+from io_aware_exact_19_amd import inputs
+from tests.parity import announce
+
+pytestmark = pytest.mark.gpu
+
+FP8_MAX_ABS = 0.25
+FP8_MEAN_ABS = 1e-2
+LSE_ABS = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    fa.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(B, H, nq, nk, causal, W, seed, q_mult=1.0, rows=None):
+    q8, k8, v8, dq, dk, dv = inputs.fp8_qkv(B, nq, nk, H, 128, seed, q_mult)
+    s = 1.0 / math.sqrt(128)
+    what = f"fp8 B{B} H{H} nq{nq} nk{nk} causal{int(causal)} W{W} x{q_mult}"
+    announce(what)
+    o, lse = fa.attention_fp8(q8.cuda(), k8.cuda(), v8.cuda(), dq.cuda(), dk.cuda(), dv.cuda(),
+                              scale=s, causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o = o.cpu().float().double().numpy()
+    lse = lse.cpu().double().numpy()
+    o_ref, lse_ref = oracle.attention_fp8(q8.numpy(), k8.numpy(), v8.numpy(), dq.numpy(),
+                                          dk.numpy(), dv.numpy(), s, causal, W)
+    assert np.all(np.isfinite(o)), what
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: -inf rows differ"
+    err = np.abs(o - o_ref)
+    lerr = float(np.abs(lse[~empty] - lse_ref[~empty]).max()) if (~empty).any() else 0.0
+    print(f"[parity] {what}: O max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
+          f"(|O| max {np.abs(o_ref).max():.2f}); lse max-abs {lerr:.3e}", file=sys.stderr,
+          flush=True)
+    assert err.max() <= FP8_MAX_ABS, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= FP8_MEAN_ABS, f"{what}: mean-abs {err.mean():.3e}"
+    assert lerr <= LSE_ABS, f"{what}: lse {lerr:.3e}"
+    return o, lse, o_ref, lse_ref
+
+
+@pytest.mark.parametrize("B,H,nq,nk,causal,W", [
+    (1, 2, 300, 300, False, -1),
+    (2, 3, 300, 300, True, -1),
+    (1, 2, 333, 200, True, -1),    # n_q > n_k: the first rows see no key
+    (1, 2, 200, 333, True, -1),    # bottom-right causal
+    (1, 2, 700, 700, True, 100),   # window: first needed tile > 0
+    (2, 2, 600, 600, False, 150),  # window without causal
+    (1, 1, 1, 700, True, -1),      # one query against 700 keys
+    (1, 2, 65, 65, False, -1),     # ragged single tiles
+    (1, 1, 129, 1100, False, -1),  # ragged keys, several tiles
+])
+def test_fp8_small(B, H, nq, nk, causal, W):
+    _run(B, H, nq, nk, causal, W, seed=21)
+
+
+def test_fp8_peaked():
+    _run(1, 4, 512, 512, False, -1, seed=22, q_mult=4.0)
+
+
+def test_fp8_rows_without_keys():
+    o, lse, _, _ = _run(1, 2, 333, 200, True, -1, seed=23)
+    assert np.all(o[:, :133] == 0)
+    assert np.all(np.isneginf(lse[:, :, :133]))
+
+
+def test_fp8_no_keys_at_all():
+    q8, _, _, dq, _, _ = inputs.fp8_qkv(2, 5, 1, 3, 128, 24)
+    k8 = torch.empty((2, 0, 3, 128), dtype=torch.uint8, device="cuda")
+    announce("fp8 seqlen_k=0")
+    o, lse = fa.attention_fp8(q8.cuda(), k8, k8.clone(), dq.cuda(), dq.cuda(), dq.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("causal,q_mult", [(False, 1.0), (True, 4.0)])
+def test_fp8_workload_prefill_2k(causal, q_mult):
+    """The bf16 headline shape (B4 H16 N2048 d128) on e4m3 inputs, every output."""
+    _run(4, 16, 2048, 2048, causal, -1, seed=25, q_mult=q_mult)
