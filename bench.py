@@ -56,6 +56,7 @@ PEAK_FP8_TFLOPS = 5000.0    # dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
+FP8_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_fp8.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_mfma_util.txt")
@@ -425,11 +426,13 @@ def pmc_summary(fetch_dir, write_dir, target, out_path, cmd):
     print("\n".join(lines))
 
 
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
-                 "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                 "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE")
 
 def _kernel_short(name):
-    return name.replace("void fa::(anonymous namespace)::", "").split("(fa::")[0]
+    name = name.replace("void ", "", 1) if name.startswith("void ") else name
+    return name.replace("fa::(anonymous namespace)::", "").split("(")[0]
 
 
 def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
@@ -466,9 +469,11 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
                 lines.append(f"  {c}: {med[c]:.0f}")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
             lines.append(f"  mfma_flops_bf16: {med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.0f}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_F8" in med:
+            lines.append(f"  mfma_flops_f8: {med['SQ_INSTS_VALU_MFMA_MOPS_F8'] * 512:.0f}")
         if k in dur:
             lines.append(f"  dispatch_us_under_counters: {statistics.median(dur[k]) * 1e6:.2f}")
-    src = PREFILL_KERNEL_SRC
+    src = FP8_KERNEL_SRC if target.startswith("fp8") else PREFILL_KERNEL_SRC
     lines.append(f"kernel_source_sha256: {sha256(src)}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
