@@ -231,20 +231,17 @@ def make_backward(torch, fa, inputs, configs, cfg, causal=False):
 
 
 def make_fp8(torch, fa, inputs, configs, cfg, causal=False):
-    """The headline shape on e4m3 inputs with per-(batch, head) factors; one
-    call = the V transpose into the workspace plus the forward kernel."""
+    """The headline shape on e4m3 inputs with per-(batch, head) factors."""
     B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
     q8, k8, v8, dq, dk, dv = (x.cuda() for x in inputs.fp8_qkv(B, N, N, H, d, cfg["seed"]))
     o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    need = fa.fa_fwd_fp8_workspace_size(B, H, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     s = configs.default_scale(d)
     stream = torch.cuda.current_stream()
 
     def launch():
-        st = fa.fa_fwd_fp8(q8, k8, v8, o, lse, dq, dk, dv, B, H, N, N, d, s, int(causal), -1, ws,
-                           need, stream)
+        st = fa.fa_fwd_fp8(q8, k8, v8, o, lse, dq, dk, dv, B, H, N, N, d, s, int(causal), -1,
+                           stream)
         if st != 0:
             raise fa.FAError(st, "fa_fwd_fp8")
 
@@ -254,7 +251,7 @@ def make_fp8(torch, fa, inputs, configs, cfg, causal=False):
                 inputs="e4m3 codes, one factor per (batch, head)", output="bf16")
     w = Workload(name, launch, 4 * d * H * B * pairs, "TFLOP/s", PEAK_FP8_TFLOPS, "mfma",
                  "fp8-e4m3", conf)
-    w.tensors = (q8, k8, v8, dq, dk, dv, ws)
+    w.tensors = (q8, k8, v8, dq, dk, dv)
     return w
 
 

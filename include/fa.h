@@ -175,13 +175,6 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
               int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_fwd_fp8_workspace_size -- bytes of device workspace fa_fwd_fp8 needs:
- * the transposed V, batch * heads * d * ceil(seqlen_k / 64) * 64 bytes.
- * 0 when any size is <= 0 or d != 128.
- */
-size_t fa_fwd_fp8_workspace_size(int batch, int heads, int seqlen_k, int d);
-
-/*
  * fa_fwd_fp8 -- attention forward (dense) on 8-bit floating-point inputs, the
  * low-precision variant named in "FlashAttention" (aiwiki.page), section
  * "Versions".  q, k, v hold OCP e4m3 codes (1 byte each, the float8_e4m3fn
@@ -198,16 +191,13 @@ size_t fa_fwd_fp8_workspace_size(int batch, int heads, int seqlen_k, int d);
  * the P V product, O divided by the sum of exactly those rounded
  * probabilities (so each output row is a convex combination of V rows),
  * lse from the unrounded sum.
- * workspace: device, 16-byte aligned, >= fa_fwd_fp8_workspace_size(); it
- * receives V transposed to [batch, heads, d, keys] (contents on return are
- * unspecified; may be NULL when seqlen_k == 0).  FA_ERR_UNSUPPORTED for
- * d != 128, more than 65535 (batch, head) pairs, or key rows and transposed
- * blocks past 32-bit offsets.
+ * No workspace.  FA_ERR_UNSUPPORTED for d != 128 or when 64 rows of
+ * heads * d bytes reach 4 GiB.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* descale_q, const float* descale_k, const float* descale_v, int batch,
                int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
-               int window_left, void* workspace, size_t workspace_bytes, void* stream);
+               int window_left, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fa_status_string(int status);

@@ -25,7 +25,6 @@ from .binding import (  # noqa: F401
     fa_fwd,
     fa_fwd_fp32,
     fa_fwd_fp8,
-    fa_fwd_fp8_workspace_size,
     fa_fwd_kvcache,
     fa_status_string,
     load_library,

@@ -30,8 +30,7 @@ FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_decode_workspace_size", "fa_decode", "fa_fwd_fp8_workspace_size", "fa_fwd_fp8",
-            "fa_status_string")
+            "fa_decode_workspace_size", "fa_decode", "fa_fwd_fp8", "fa_status_string")
 
 _lib = None
 
@@ -68,9 +67,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_size.restype = Z
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode.restype = I
-    lib.fa_fwd_fp8_workspace_size.argtypes = [I, I, I, I]
-    lib.fa_fwd_fp8_workspace_size.restype = Z
-    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, Z, P]
+    lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_fwd_fp8.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -142,16 +139,12 @@ def fa_decode(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d, 
                                     _ptr(workspace), workspace_bytes, _stream(stream))
 
 
-def fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d) -> int:
-    return int(load_library().fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d))
-
-
 def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, batch, heads, seqlen_q, seqlen_k,
-               d, scale, causal, window_left, workspace, workspace_bytes, stream=None) -> int:
+               d, scale, causal, window_left, stream=None) -> int:
     return load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                      _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), batch,
                                      heads, seqlen_q, seqlen_k, d, scale, int(causal), window_left,
-                                     _ptr(workspace), workspace_bytes, _stream(stream))
+                                     _stream(stream))
 
 
 def fa_status_string(status: int) -> str:
@@ -308,7 +301,7 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale=None, chunk=256, workspace=N
 
 
 def attention_fp8(q, k, v, descale_q, descale_k, descale_v, *, scale=None, causal=False,
-                  window_left=-1, return_lse=True, workspace=None, stream=None):
+                  window_left=-1, return_lse=True, stream=None):
     """Dense attention on e4m3 codes: q [B, n_q, H, 128], k/v [B, n_k, H, 128]
     torch.uint8 (or torch.float8_e4m3fn) on the GPU, descale_* fp32 [B * H]
     (or [B, H]).  Returns (o [B, n_q, H, 128] bf16, lse [B, H, n_q] fp32 or None)."""
@@ -328,13 +321,9 @@ def attention_fp8(q, k, v, descale_q, descale_k, descale_v, *, scale=None, causa
         ds.append(t)
     o = torch.empty((B, n_q, H, d), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if return_lse else None
-    need = fa_fwd_fp8_workspace_size(B, H, n_k, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = fa_fwd_fp8(q, k, v, o, lse, ds[0], ds[1], ds[2], B, H, n_q, n_k, d, s, int(causal),
-                    int(window_left), workspace, workspace.numel() * workspace.element_size(),
-                    stream)
+                    int(window_left), stream)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
     return o, lse

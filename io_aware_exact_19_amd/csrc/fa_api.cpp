@@ -202,15 +202,10 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-size_t fa_fwd_fp8_workspace_size(int batch, int heads, int seqlen_k, int d) {
-  if (batch <= 0 || heads <= 0 || seqlen_k <= 0 || d != 128) return 0;
-  return fa::fp8_workspace_bytes(batch, heads, seqlen_k, d);
-}
-
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* descale_q, const float* descale_k, const float* descale_v, int batch,
                int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
-               int window_left, void* workspace, size_t workspace_bytes, void* stream) {
+               int window_left, void* stream) {
   if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0 || d <= 0) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
@@ -224,18 +219,11 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
       !aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4))
     return FA_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_fwd_fp8_workspace_size(batch, heads, seqlen_k, d);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
-    return FA_ERR_WORKSPACE;
-  // 32-bit offsets: 64 key rows of K, 32 query rows, and one head's
-  // transposed V block (d x padded keys) must each stay below 4 GiB
+  // 32-bit offsets: 64 key rows of K or V and 32 query rows stay below 4 GiB
   const unsigned long long row_bytes = (unsigned long long)heads * d;
-  const unsigned long long n_kpad = ((unsigned long long)seqlen_k + 63) / 64 * 64;
-  if (row_bytes * 64 >= 0x100000000ull || n_kpad * d >= 0x100000000ull) return FA_ERR_UNSUPPORTED;
+  if (row_bytes * 64 >= 0x100000000ull) return FA_ERR_UNSUPPORTED;
   const long long grid = (long long)batch * heads * ((seqlen_q + 127) / 128);
-  if (grid > 0x7fffffffLL || (long long)batch * heads * (long long)(n_kpad / 64) > 0x7fffffffLL ||
-      (long long)batch * heads > 65535)
-    return FA_ERR_UNSUPPORTED;
+  if (grid > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
 
   fa::Fp8LaunchArgs a;
   a.q = q;
@@ -253,7 +241,6 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   a.scale = scale;
   a.causal = causal;
   a.window_left = window_left;
-  a.workspace = workspace;
   const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -18,8 +18,10 @@
 //    64-key tile, in register order, which is exactly the k operand layout of
 //    the P V product: no data movement between the two products.
 //  * The P V operand then wants 32 consecutive keys of one head dimension:
-//    V is transposed once per call into a workspace Vt [batch, heads, d,
-//    n_kpad] (a pass over V), so both tiles stream into LDS as plain rows.
+//    the V tile stays row-major in LDS and four 8-bit transposing reads
+//    (ds_read_b64_tr_b8: in each 16-lane group lane j addresses row j / 2,
+//    bytes 8 (j % 2), and receives byte column j of the 8 x 16 block, rows in
+//    order) gather 8 keys each.
 //  * The row sums of the rounded probabilities come from one more matrix
 //    product per tile (an operand of e4m3 ones), not from vector work.
 //  * The first product of each score chain takes a zero block held in
@@ -54,53 +56,26 @@ __device__ __forceinline__ f32x16_t mma8(const i32x8_t& a, const i32x8_t& b, con
 // LDS position of 16-byte chunk c of K tile row r (8 chunks per 128-byte row):
 // the 16 rows one 16-lane group reads land in distinct bank groups
 __device__ __forceinline__ int k8_swz(int r) { return ((r >> 1) & 3) | ((r >> 3) & 4); }
-// Vt tile row c (head dimension), 4 chunks per 64-byte row
-__device__ __forceinline__ int v8_swz(int c) { return (c >> 2) & 3; }
+// V tile row r (key): the 8 rows one 16-lane transposing read covers land in
+// distinct bank groups
+__device__ __forceinline__ int v8_swz(int r) { return (r >> 1) & 3; }
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 
 struct Fp8Args {
   const uint8_t* q;     // [batch, seqlen_q, heads, 128] e4m3
   const uint8_t* k;     // [batch, seqlen_k, heads, 128] e4m3
-  const uint8_t* vt;    // [batch, heads, 128, n_kpad] e4m3 (transposed V, zero padded)
+  const uint8_t* v;     // [batch, seqlen_k, heads, 128] e4m3
   uint16_t* o;          // [batch, seqlen_q, heads, 128] bf16
   float* lse;           // [batch, heads, seqlen_q] or null
   const float* dq;      // [batch * heads] dequantisation factors
   const float* dk;
   const float* dv;
-  int batch, heads, seqlen_q, seqlen_k, n_kpad;
+  int batch, heads, seqlen_q, seqlen_k;
   float scale_log2;     // scale * log2(e)
   int causal, window_left;
 };
-
-// V [batch, n_k, heads, 128] -> Vt [batch, heads, 128, n_kpad], keys past n_k zero.
-// One workgroup per (64-key block, batch * head).
-__global__ __launch_bounds__(256) void transpose_v_kernel(const uint8_t* v, uint8_t* vt, int heads,
-                                                         int n_k, int n_kpad) {
-  __shared__ uint8_t tile[kBC8][kD8 + 4];
-  const int bh = blockIdx.y, b = bh / heads, h = bh - b * heads;
-  const int k0 = blockIdx.x * kBC8, tid = threadIdx.x;
-  const long long row_stride = (long long)heads * kD8;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int s = i * 256 + tid, r = s >> 3, c = (s & 7) * 16;
-    u32x4_t x = {0u, 0u, 0u, 0u};
-    if (k0 + r < n_k) x = *(const u32x4_t*)(v + ((long long)b * n_k + k0 + r) * row_stride + h * kD8 + c);
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      *(uint32_t*)&tile[r][c + 4 * w] = x[w];
-  }
-  __syncthreads();
-  uint8_t* dst = vt + (long long)bh * kD8 * n_kpad + k0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int s = i * 256 + tid, c = s >> 2, ch = (s & 3) * 16;
-    u32x4_t y;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      y[w] = (uint32_t)tile[ch + 4 * w][c] | ((uint32_t)tile[ch + 4 * w + 1][c] << 8) |
-             ((uint32_t)tile[ch + 4 * w + 2][c] << 16) | ((uint32_t)tile[ch + 4 * w + 3][c] << 24);
-    *(u32x4_t*)(dst + (long long)c * n_kpad + ch) = y;
-  }
-}
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -131,7 +106,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
   const uint32_t row_bytes = (uint32_t)(a.heads * kD8);
   const uint8_t* qg = a.q + ((long long)b * n_q * a.heads + h) * kD8;
   const uint8_t* kg = a.k + ((long long)b * n_k * a.heads + h) * kD8;
-  const uint8_t* vtg = a.vt + (long long)bh * kD8 * a.n_kpad;
+  const uint8_t* vg = a.v + ((long long)b * n_k * a.heads + h) * kD8;
   uint16_t* og = a.o + ((long long)b * n_q * a.heads + h) * kD8;
 
   const int q0 = qt * kRows8;
@@ -175,18 +150,17 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kg + (long long)k0 * row_bytes), 0, nrec, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)vtg, 0, (uint32_t)(kD8 * a.n_kpad), kRsrcWord3);
+        (void*)(vg + (long long)k0 * row_bytes), 0, nrec, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < kLoads8; ++i) {
       const int blk = i * kWaves8 + wave;
       const int s = blk * 64 + lane;
-      const int r = s >> 3, ck = (s & 7) ^ k8_swz(r);
-      const int c = s >> 2, cv = (s & 3) ^ v8_swz(c);
+      const int r = s >> 3;
+      const int ck = (s & 7) ^ k8_swz(r), cv = ((s & 7) ^ v8_swz(r)) & 7;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + blk * 1024), 16,
                                                (uint32_t)r * row_bytes + (uint32_t)ck * 16, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + blk * 1024), 16,
-                                               (uint32_t)c * a.n_kpad + (uint32_t)(k0 + cv * 16), 0,
-                                               0, 0);
+                                               (uint32_t)r * row_bytes + (uint32_t)cv * 16, 0, 0, 0);
     }
   };
 
@@ -204,14 +178,21 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
         k_off[kb][kk][p] = r * kD8 + ((c ^ k8_swz(r)) & 7) * 16;
       }
   }
-  int v_off[4][2];  // [db][16-byte piece]
+  // V^T fragment of block db, piece t: lane j of 16-lane group g reads row
+  // 32 (g / 2) + 8 t + j / 2, bytes 8 (j % 2) of chunk 2 db + g % 2, and
+  // receives keys 32 (g / 2) + 8 t + [0, 8) of head dimension 32 db + 16 (g % 2) + j
+  int v_off[4][4];  // [db][t]
+  {
+    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int c = 32 * db + l32, ch = 2 * half + p;
-      v_off[db][p] = c * kBC8 + ((ch ^ v8_swz(c)) & 3) * 16;
-    }
+      for (int t = 0; t < 4; ++t) {
+        const int r = 32 * (g >> 1) + 8 * t + (j >> 1);
+        const int ch = 2 * db + (g & 1);
+        v_off[db][t] = r * kD8 + ((ch ^ v8_swz(r)) & 7) * 16 + 8 * (j & 1);
+      }
+  }
 
   f32x16_t zero;  // accumulator input of each chain's first product (see header)
 #pragma unroll
@@ -318,8 +299,16 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
       pf[w] = (int)pack_fp8x4(p[kb][r], p[kb][r + 1], p[kb][r + 2], p[kb][r + 3]);
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      oacc[db] = mma8(frag(vl, v_off[db][0], v_off[db][1]), pf, oacc[db]);
+    for (int db = 0; db < 4; ++db) {
+      i32x8_t vf;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x2_t x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vl + v_off[db][t]));
+        vf[2 * t] = x[0];
+        vf[2 * t + 1] = x[1];
+      }
+      oacc[db] = mma8(vf, pf, oacc[db]);
+    }
     osum = mma8(ones, pf, osum);
   };
 
@@ -365,26 +354,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
 
 }  // namespace
 
-size_t fp8_workspace_bytes(int batch, int heads, int seqlen_k, int d) {
-  const size_t n_kpad = (size_t)ceil_div(seqlen_k, kBC8) * kBC8;
-  return (size_t)batch * heads * d * n_kpad;
-}
-
 hipError_t launch_fwd_fp8(const Fp8LaunchArgs& p, hipStream_t stream) {
-  const int n_kpad = ceil_div(p.seqlen_k, kBC8) * kBC8;
   const long long bh = (long long)p.batch * p.heads;
   if (bh <= 0 || p.seqlen_q <= 0) return hipSuccess;
-  if (n_kpad > 0) {
-    hipLaunchKernelGGL(transpose_v_kernel, dim3((unsigned)(n_kpad / kBC8), (unsigned)bh), dim3(256), 0,
-                       stream, (const uint8_t*)p.v, (uint8_t*)p.workspace, p.heads, p.seqlen_k,
-                       n_kpad);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   Fp8Args a;
   a.q = (const uint8_t*)p.q;
   a.k = (const uint8_t*)p.k;
-  a.vt = (const uint8_t*)p.workspace;
+  a.v = (const uint8_t*)p.v;
   a.o = (uint16_t*)p.o;
   a.lse = p.lse;
   a.dq = p.descale_q;
@@ -394,7 +370,6 @@ hipError_t launch_fwd_fp8(const Fp8LaunchArgs& p, hipStream_t stream) {
   a.heads = p.heads;
   a.seqlen_q = p.seqlen_q;
   a.seqlen_k = p.seqlen_k;
-  a.n_kpad = n_kpad;
   a.scale_log2 = p.scale * kLog2e;
   a.causal = p.causal;
   a.window_left = p.window_left < 0 ? -1 : p.window_left;

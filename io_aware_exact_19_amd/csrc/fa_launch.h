@@ -89,10 +89,8 @@ struct Fp8LaunchArgs {
   int batch, heads, seqlen_q, seqlen_k;
   float scale;
   int causal, window_left;
-  void* workspace;           // >= fp8_workspace_bytes(...): transposed V
 };
 
-size_t fp8_workspace_bytes(int batch, int heads, int seqlen_k, int d);
 hipError_t launch_fwd_fp8(const Fp8LaunchArgs& p, hipStream_t stream);
 
 }  // namespace fa

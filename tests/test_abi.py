@@ -123,9 +123,7 @@ def _dec(**kw):
     # one 512-key chunk of 16384 heads x 128 dims spans 2 GiB of cache rows
     (dict(batch=1, heads=16384, max_len=512, chunk=512), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
-    (dict(workspace=0), fa.FA_ERR_WORKSPACE),
     (dict(workspace_bytes=16), fa.FA_ERR_WORKSPACE),
-    (dict(workspace=P + 4), fa.FA_ERR_WORKSPACE),
 ])
 def test_decode_rejects(lib, bad, code):
     assert _dec(**bad) == code
@@ -174,7 +172,6 @@ def _bwd(**kw):
     (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(workspace=0), fa.FA_ERR_WORKSPACE),
     (dict(workspace_bytes=2 * 2 * 4 * 64 * 4 - 1), fa.FA_ERR_WORKSPACE),
     (dict(batch=0), fa.FA_OK),
 ])
@@ -218,7 +215,7 @@ def test_binding_fails_loudly_without_library(tmp_path):
 def _fp8(**kw):
     args = dict(q=P, k=P, v=P, o=P, lse=P, descale_q=P, descale_k=P, descale_v=P, batch=2,
                 heads=4, seqlen_q=64, seqlen_k=100, d=128, scale=0.125, causal=0, window_left=-1,
-                workspace=P, workspace_bytes=1 << 30, stream=NULL_STREAM)
+                stream=NULL_STREAM)
     args.update(kw)
     return fa.fa_fwd_fp8(**args)
 
@@ -240,21 +237,10 @@ def _fp8(**kw):
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),
-    (dict(workspace=0), fa.FA_ERR_WORKSPACE),
-    (dict(workspace=P + 4), fa.FA_ERR_WORKSPACE),
-    (dict(workspace_bytes=2 * 4 * 128 * 128 - 1), fa.FA_ERR_WORKSPACE),
-    (dict(batch=300, heads=300, workspace_bytes=1 << 40), fa.FA_ERR_UNSUPPORTED),
+    (dict(heads=1 << 19), fa.FA_ERR_UNSUPPORTED),  # 64 rows of heads * 128 bytes reach 4 GiB
 ])
 def test_fwd_fp8_rejects(lib, bad, code):
     assert _fp8(**bad) == code
-
-
-def test_fwd_fp8_workspace_size(lib):
-    # V transposed to [batch, heads, d, keys rounded up to 64]
-    assert fa.fa_fwd_fp8_workspace_size(2, 4, 100, 128) == 2 * 4 * 128 * 128
-    assert fa.fa_fwd_fp8_workspace_size(1, 1, 64, 128) == 128 * 64
-    assert fa.fa_fwd_fp8_workspace_size(1, 1, 0, 128) == 0
-    assert fa.fa_fwd_fp8_workspace_size(1, 1, 64, 64) == 0
 
 
 @pytest.mark.parametrize("empty", [dict(batch=0), dict(heads=0), dict(seqlen_q=0)])
