@@ -92,12 +92,27 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // work item: (batch, head, query tile); tiles of one head on one XCD,
-  // causal heads start their longest tiles first
+  // work item: (batch, head, query tile).  Workgroup i reaches XCD i % 8,
+  // which starts its workgroups in order as CUs free up; every head keeps its
+  // tiles on one XCD (shared L2).  With a mask the tiles differ in length:
+  // XCD x takes the heads x, x + 8, ... and starts all their tiles longest
+  // first (longest-processing-time order); otherwise the ids are numbered
+  // XCD-contiguously.
   const int nqt = ceil_div(a.seqlen_q, kRows8);
-  const int id = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int bh = id / nqt, t = id - bh * nqt;
+  const int nbh = a.batch * a.heads;
+  int bh, t;  // t: rank of the tile in start order
+  if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
+    const int x = blockIdx.x & 7, kx = blockIdx.x >> 3, hx = nbh >> 3;
+    t = kx / hx;
+    bh = x + 8 * (kx - t * hx);
+  } else {
+    const int id = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = id / nqt;
+    t = id - bh * nqt;
+  }
   const int b = bh / a.heads, h = bh - b * a.heads;
+  // causal: later tiles see more keys; a left window without the causal
+  // bound: earlier tiles see more keys
   const int qt = a.causal || a.window_left < 0 ? nqt - 1 - t : t;
   const int n_q = a.seqlen_q, n_k = a.seqlen_k, delta = n_k - n_q;
   const int causal = a.causal, W = a.window_left;

@@ -81,6 +81,11 @@ def _run(B, H, nq, nk, causal, W, seed, q_mult=1.0, rows=None):
     (1, 1, 1, 700, True, -1),      # one query against 700 keys
     (1, 2, 65, 65, False, -1),     # ragged single tiles
     (1, 1, 129, 1100, False, -1),  # ragged keys, several tiles
+    # batch * heads divisible by 8: masked tiles start longest first across heads
+    (2, 4, 300, 300, True, -1),
+    (1, 8, 333, 200, True, -1),
+    (2, 4, 520, 520, True, 200),
+    (1, 8, 400, 400, False, 100),  # window without causal: earliest tiles first
 ])
 def test_fp8_small(B, H, nq, nk, causal, W):
     _run(B, H, nq, nk, causal, W, seed=21)
