@@ -57,6 +57,7 @@ PEAK_HBM_GBS = 8000.0
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
 FP8_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_fp8.hip")
+BACKWARD_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_backward.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_mfma_util.txt")
@@ -470,7 +471,9 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
             lines.append(f"  mfma_flops_f8: {med['SQ_INSTS_VALU_MFMA_MOPS_F8'] * 512:.0f}")
         if k in dur:
             lines.append(f"  dispatch_us_under_counters: {statistics.median(dur[k]) * 1e6:.2f}")
-    src = FP8_KERNEL_SRC if target.startswith("fp8") else PREFILL_KERNEL_SRC
+    src = (FP8_KERNEL_SRC if target.startswith("fp8") else
+           BACKWARD_KERNEL_SRC if target.startswith("backward") else PREFILL_KERNEL_SRC)
+    lines.append(f"kernel_source: {os.path.relpath(src, ROOT)}")
     lines.append(f"kernel_source_sha256: {sha256(src)}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
