@@ -43,7 +43,7 @@ constexpr int kBC8 = 64;            // keys per tile
 constexpr int kWaves8 = 4;
 constexpr int kThreads8 = kWaves8 * 64;
 constexpr int kRows8 = kWaves8 * 32;  // query rows per workgroup
-constexpr int kTile8 = kBC8 * kD8;    // bytes of one K or Vt tile (8 KB)
+constexpr int kTile8 = kBC8 * kD8;    // bytes of one K or V tile (8 KB)
 constexpr int kLoads8 = kTile8 / 16 / kThreads8;  // 16-byte loads per thread per tile
 constexpr int kRsrcWord3 = 0x00020000;            // raw buffer, 32-bit data format
 constexpr float kLazyBound8 = 256.0f;  // probabilities stay <= 2^8, inside e4m3's 448
