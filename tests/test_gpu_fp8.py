@@ -114,3 +114,32 @@ def test_fp8_no_keys_at_all():
 def test_fp8_workload_prefill_2k(causal, q_mult):
     """The bf16 headline shape (B4 H16 N2048 d128) on e4m3 inputs, every output."""
     _run(4, 16, 2048, 2048, causal, -1, seed=25, q_mult=q_mult)
+
+
+def test_fp8_long_prompt_sampled_rows():
+    """B1 H32 N8000 causal on e4m3 inputs (ragged last query and key tiles,
+    several rounds of workgroups): sampled rows of every head."""
+    B, H, N, d = 1, 32, 8000, 128
+    q8, k8, v8, dq, dk, dv = inputs.fp8_qkv(B, N, N, H, d, seed=26)
+    s = 1.0 / math.sqrt(d)
+    announce("fp8 long 8k causal")
+    o, lse = fa.attention_fp8(q8.cuda(), k8.cuda(), v8.cuda(), dq.cuda(), dk.cuda(), dv.cuda(),
+                              scale=s, causal=True)
+    torch.cuda.synchronize()
+    o = o.cpu().float().double().numpy()
+    lse = lse.cpu().double().numpy()
+    rng = np.random.default_rng(4)
+    rows = np.array(sorted(set([0, 1, 63, 64, 127, 128, 3999, 4000, 7871, 7872, 7935, 7936, 7999]
+                               + list(rng.integers(0, N, 16)))))
+    f = lambda codes, ds: oracle.e4m3_decode(codes.numpy()) * ds.double().numpy().reshape(B, 1, H, 1)
+    qn, kn, vn = f(q8, dq), f(k8, dk), f(v8, dv)
+    o_ref = np.zeros((len(rows), H, d))
+    lse_ref = np.zeros((H, len(rows)))
+    for h in range(H):
+        o_ref[:, h], lse_ref[h] = oracle.sdpa(qn[0, rows, h], kn[0, :, h], vn[0, :, h], s, True,
+                                             q_index=rows, n_q=N)
+    err = np.abs(o[0, rows] - o_ref)
+    lerr = np.abs(lse[0][:, rows] - lse_ref).max()
+    print(f"[parity] fp8 long 8k sampled rows: O max-abs {err.max():.3e} mean-abs {err.mean():.3e};"
+          f" lse max-abs {lerr:.3e}", file=sys.stderr, flush=True)
+    assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS and lerr <= LSE_ABS
