@@ -8,7 +8,8 @@ algorithmic throughput (4 * d FLOPs per allowed (query, key) pair) over K
 timed steps.  The line also carries:
 
 * ``roofline``: the prefill kernel's algorithmic FLOPs per launch divided by
-  its mean launch duration (HIP events on the launch stream) against the
+  its mean launch duration (a pair of HIP events on the launch stream around
+  the timed launches) against the
   dense bf16 matrix-core peak, plus the HBM traffic per launch read from the
   committed rocprofv3 counter summary when it was taken on the current kernel
   source (else null);
@@ -277,26 +278,44 @@ def settle(torch, w, ms):
 
 
 def time_launches(torch, w, steps, warmup, settle_ms=0.0):
-    """Let the clock settle, warm up, then time exactly ``steps`` launches:
-    wall clock between two device synchronisations, and per-launch HIP events
-    on the launch stream."""
+    """Let the clock settle, warm up, then time exactly ``steps`` back-to-back
+    launches between two device synchronisations: wall clock, and one pair of
+    HIP events on the launch stream around the same region (mean launch
+    duration = event time / steps).  Events recorded around every launch
+    would add two queue packets per step (measured: +7 us of wall time and
+    +2 us of event time per 130 us launch), so the spread comes from a
+    second pass after the timed one, event pairs around chunks of launches.
+    Returns (wall ms per step, event ms per step, fastest chunk's ms per
+    launch)."""
     if settle_ms > 0:
         settle(torch, w, settle_ms)
     for _ in range(warmup):
         w.launch()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         w.launch()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
-    return (t1 - t0) * 1e3 / steps, statistics.mean(per), min(per)
+    wall_ms = (t1 - t0) * 1e3 / steps
+    event_ms = start.elapsed_time(end) / steps
+    # spread (not part of the timed region): chunks of up to 10 launches
+    chunk = max(1, min(10, steps // 2))
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for i in range(5):
+        starts[i].record()
+        for _ in range(chunk):
+            w.launch()
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) / chunk for a, b in zip(starts, ends)]  # ms per launch
+    return wall_ms, event_ms, min(per)
 
 
 def rate(w, ms):
