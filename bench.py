@@ -285,8 +285,9 @@ def time_launches(torch, w, steps, warmup, settle_ms=0.0):
     would add two queue packets per step (measured: +7 us of wall time and
     +2 us of event time per 130 us launch), so the spread comes from a
     second pass after the timed one, event pairs around chunks of launches.
-    Returns (wall ms per step, event ms per step, fastest chunk's ms per
-    launch)."""
+    Returns (wall ms per step, event ms per step, [fastest, slowest] chunk's
+    ms per launch); a chunk carries its own event overhead, so on short
+    kernels even the fastest chunk can sit above the timed mean."""
     if settle_ms > 0:
         settle(torch, w, settle_ms)
     for _ in range(warmup):
@@ -315,7 +316,7 @@ def time_launches(torch, w, steps, warmup, settle_ms=0.0):
         ends[i].record()
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) / chunk for a, b in zip(starts, ends)]  # ms per launch
-    return wall_ms, event_ms, min(per)
+    return wall_ms, event_ms, [round(min(per), 5), round(max(per), 5)]
 
 
 def rate(w, ms):
@@ -593,7 +594,7 @@ def main():
 
     if args.profile_target:
         w = builders[args.profile_target]()
-        wall, mean_ms, min_ms = time_launches(torch, w, args.steps, args.warmup, args.settle_ms)
+        wall, mean_ms, chunks = time_launches(torch, w, args.steps, args.warmup, args.settle_ms)
         log(f"[profile] {w.name}: {args.steps} launches, mean {mean_ms:.4f} ms, "
             f"{rate(w, mean_ms):.2f} {w.unit}")
         if args.calibrate_copy:
@@ -610,7 +611,7 @@ def main():
     head = builders["prefill_2k"]()
     log(f"[bench] timing {head.name}: settle {args.settle_ms:.0f} ms, warmup {args.warmup}, "
         f"steps {args.steps}")
-    wall_ms, mean_ms, min_ms = time_launches(torch, head, args.steps, args.warmup, args.settle_ms)
+    wall_ms, mean_ms, chunks = time_launches(torch, head, args.steps, args.warmup, args.settle_ms)
     achieved = rate(head, mean_ms)
     traffic = read_traffic(TRAFFIC_SUMMARY, PREFILL_KERNEL_SRC)
     result = {
@@ -639,7 +640,7 @@ def main():
             "kernel": "fwd_bf16_kernel<128,false>",
             "flops_per_launch": head.work,
             "mean_launch_ms": round(mean_ms, 5),
-            "min_launch_ms": round(min_ms, 5),
+            "chunk_ms_range": chunks,
         },
     }
     log(f"[bench] {head.name}: {result['value']} TFLOP/s wall, kernel {achieved:.1f} TFLOP/s")
@@ -653,12 +654,12 @@ def main():
             w = builders[key]()
             steps = 20 if key != "decode" else 10
             log(f"[bench] timing {w.name}")
-            wall, mean2, min2 = time_launches(torch, w, steps, 3, args.settle_ms)
+            wall, mean2, chunks2 = time_launches(torch, w, steps, 3, args.settle_ms)
             r = rate(w, mean2)
             entry = {"workload": w.name, "value": round(r, 3), "unit": w.unit,
                      "frac_of_peak": round(r / w.peak, 4), "peak": w.peak, "bound": w.bound,
                      "dtype": w.dtype, "mean_launch_ms": round(mean2, 5),
-                     "min_launch_ms": round(min2, 5), "steps": steps}
+                     "chunk_ms_range": chunks2, "steps": steps}
             if key == "decode":
                 entry["kv_bytes_per_launch"] = w.config["kv_bytes"]
                 entry["traffic"] = read_traffic(DECODE_TRAFFIC_SUMMARY, DECODE_KERNEL_SRC)
