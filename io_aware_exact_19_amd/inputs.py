@@ -85,10 +85,11 @@ def decode_cache(batch, max_len, heads, d, seqlens, seed, device, name, dtype=to
     return cache
 
 
-def fp8_tensor(shape, seed: int, mult: float = 1.0):
+def fp8_tensor(shape, seed: int, mult: float = 1.0, device="cpu"):
     """e4m3 codes (uint8 [B, n, H, d]) and per-(batch, head) dequantisation
-    factors (float32 [B * H]) of i.i.d. N(0,1) values times ``mult``."""
-    x = normal(shape, seed, torch.float32) * mult
+    factors (float32 [B * H]) of i.i.d. N(0,1) values times ``mult``, drawn
+    on ``device``."""
+    x = normal(shape, seed, torch.float32, device) * mult
     B, _, H, _ = x.shape
     amax = x.abs().amax(dim=(1, 3))  # [B, H]
     ds = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))

@@ -143,3 +143,37 @@ def test_fp8_long_prompt_sampled_rows():
     print(f"[parity] fp8 long 8k sampled rows: O max-abs {err.max():.3e} mean-abs {err.mean():.3e};"
           f" lse max-abs {lerr:.3e}", file=sys.stderr, flush=True)
     assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS and lerr <= LSE_ABS
+
+
+def test_fp8_keys_beyond_4gib():
+    """More than 2^32 bytes of e4m3 keys (and values) at a row of 8 KiB
+    (64 heads x d 128), with a ragged last tile: each tile's descriptor is
+    rebuilt from a 64-bit base.  Generated on the device; sampled (row, head)
+    outputs checked against the oracle."""
+    B, H, d, n_q = 1, 64, 128, 64
+    n_k = 2 ** 32 // (H * d) + 1000
+    announce(f"fp8 n_q {n_q} n_k {n_k} H{H} (K, V {n_k * H * d / 2 ** 30:.2f} GiB each)")
+    q8, dq = inputs.fp8_tensor((B, n_q, H, d), inputs.subseed(27, "q"), device="cuda")
+    k8, dk = inputs.fp8_tensor((B, n_k, H, d), inputs.subseed(27, "k"), device="cuda")
+    torch.cuda.empty_cache()
+    v8, dv = inputs.fp8_tensor((B, n_k, H, d), inputs.subseed(27, "v"), device="cuda")
+    torch.cuda.empty_cache()
+    s = 1.0 / math.sqrt(d)
+    rows = np.array([0, 31, 63])
+    for causal in (False, True):
+        o, lse = fa.attention_fp8(q8, k8, v8, dq, dk, dv, scale=s, causal=causal)
+        torch.cuda.synchronize()
+        for h in (0, 37, 63):
+            dec = lambda codes, ds: oracle.e4m3_decode(codes.cpu().numpy()) * float(ds[h])
+            qn = dec(q8[0, rows, h].contiguous(), dq)
+            kn = dec(k8[0, :, h].contiguous(), dk)
+            vn = dec(v8[0, :, h].contiguous(), dv)
+            o_ref, lse_ref = oracle.sdpa(qn, kn, vn, s, causal, q_index=rows, n_q=n_q)
+            err = np.abs(o[0, rows, h].cpu().double().numpy() - o_ref)
+            lerr = np.abs(lse[0, h, rows].cpu().double().numpy() - lse_ref).max()
+            print(f"[parity] fp8 beyond 4 GiB causal{int(causal)} head {h}: O max-abs "
+                  f"{err.max():.3e} mean-abs {err.mean():.3e}; lse max-abs {lerr:.3e}",
+                  file=sys.stderr, flush=True)
+            assert err.max() <= FP8_MAX_ABS and err.mean() <= FP8_MEAN_ABS and lerr <= LSE_ABS
+    del q8, k8, v8
+    torch.cuda.empty_cache()

@@ -259,6 +259,33 @@ def test_key_range_beyond_one_buffer_window():
     torch.cuda.empty_cache()
 
 
+def test_d64_keys_beyond_4gib():
+    """More than 2^32 bytes of keys (and values) at d = 64 (128 heads, a
+    16 KiB row) with a ragged last tile: the four-wave kernel rebuilds each
+    tile's descriptor from a 64-bit base.  Generated on the device; sampled
+    (row, head) outputs checked against the oracle."""
+    H, d, n_q = 128, 64, 64
+    n_k = 2 ** 32 // (H * d * 2) + 1000
+    dev = "cuda"
+    announce(f"dense d64 n_q {n_q} n_k {n_k} H{H} (K, V {n_k * H * d * 2 / 2 ** 30:.2f} GiB each)")
+    q = inputs.normal((1, n_q, H, d), 74, device=dev)
+    k = inputs.normal((1, n_k, H, d), 75, device=dev)
+    v = inputs.normal((1, n_k, H, d), 76, device=dev)
+    s = 1.0 / math.sqrt(d)
+    rows = np.array([0, 31, 63])
+    for causal in (False, True):
+        o, lse = fa.attention(q, k, v, scale=s, causal=causal)
+        torch.cuda.synchronize()
+        for h in (0, 77, 127):
+            kh, vh = _np(k[0, :, h].cpu()), _np(v[0, :, h].cpu())
+            o_ref, lse_ref = oracle.sdpa(_np(q[0, rows, h].cpu()), kh, vh, s, causal,
+                                         q_index=rows, n_q=n_q)
+            check(o[0, rows, h].cpu(), lse[0, h, rows].cpu(), o_ref, lse_ref, torch.bfloat16,
+                  f"d64 beyond 4 GiB causal{int(causal)} head {h}")
+    del q, k, v
+    torch.cuda.empty_cache()
+
+
 def test_varlen_equals_per_sequence_dense():
     """The packed call and one dense call per sequence run the same tiles in
     the same order: identical bits."""
