@@ -12,7 +12,8 @@ timed steps.  The line also carries:
   the timed launches) against the
   dense bf16 matrix-core peak, plus the HBM traffic per launch read from the
   committed rocprofv3 counter summary when it was taken on the current kernel
-  source (else null);
+  source (else null), and the mean launch time when a 1 GiB buffer is
+  written before every launch (inputs no longer in the last-level cache);
 * ``cpu_baseline``: the fp64 CPU oracle timed on this host's cores on the
   same workload;
 * ``secondary``: the other workloads (causal 2k, 8000-token causal prompt,
@@ -319,6 +320,26 @@ def time_launches(torch, w, steps, warmup, settle_ms=0.0):
     return wall_ms, event_ms, [round(min(per), 5), round(max(per), 5)]
 
 
+def time_evicted(torch, w, launches=40, warmup=10, evict_bytes=1 << 30):
+    """Median launch time with a 1 GiB buffer written before every launch, so
+    the inputs start each launch outside the last-level cache (256 MB on
+    MI355X); event pairs around each launch alone, the buffer writes
+    outside them; the first ``warmup`` pairs are not counted."""
+    junk = torch.empty(evict_bytes, dtype=torch.uint8, device="cuda")
+    pairs = []
+    for i in range(warmup + launches):
+        junk.fill_(i & 255)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        w.launch()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    del junk
+    return statistics.median(a.elapsed_time(b) for a, b in pairs[warmup:])
+
+
 def rate(w, ms):
     scale = 1e12 if w.unit == "TFLOP/s" else 1e9
     return w.work / (ms * 1e-3) / scale
@@ -613,6 +634,7 @@ def main():
         f"steps {args.steps}")
     wall_ms, mean_ms, chunks = time_launches(torch, head, args.steps, args.warmup, args.settle_ms)
     achieved = rate(head, mean_ms)
+    evicted_ms = time_evicted(torch, head)
     traffic = read_traffic(TRAFFIC_SUMMARY, PREFILL_KERNEL_SRC)
     result = {
         "metric": METRIC,
@@ -641,6 +663,7 @@ def main():
             "flops_per_launch": head.work,
             "mean_launch_ms": round(mean_ms, 5),
             "chunk_ms_range": chunks,
+            "median_launch_ms_cache_evicted": round(evicted_ms, 5),
         },
     }
     log(f"[bench] {head.name}: {result['value']} TFLOP/s wall, kernel {achieved:.1f} TFLOP/s")
