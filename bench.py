@@ -56,6 +56,14 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix-core peak
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+# vector issue: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz, in lane
+# issue slots per second (no packed fp32 arithmetic is used)
+PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# vector issue slots per allowed (query, key) pair in the softmax: one fma
+# (scale, subtract the reference max), one exp2 (v_exp_f32 issues at half the
+# fma rate: two slots), one add (row sum), half a bf16 pack (two per
+# v_cvt_pk_bf16_f32); the count does not depend on d
+VALU_SLOTS_PER_PAIR = 4.5
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
 FP8_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_fp8.hip")
@@ -688,6 +696,15 @@ def main():
                 entry["traffic"] = read_traffic(DECODE_TRAFFIC_SUMMARY, DECODE_KERNEL_SRC)
             if key in ("varlen", "kvcache"):
                 entry["lengths"] = w.config["lengths"]
+            if key == "varlen":
+                # at d = 64 the softmax's vector work per pair equals the
+                # matrix work's share, so report the vector-issue bound too
+                pairs = w.work / (4 * w.config["d"])
+                got = pairs * VALU_SLOTS_PER_PAIR / (mean2 * 1e-3) / 1e12
+                entry["valu_roofline"] = {
+                    "bound": "alu", "achieved": round(got, 3), "peak": round(PEAK_VALU_TSLOTS, 3),
+                    "unit": "T lane-slots/s", "frac": round(got / PEAK_VALU_TSLOTS, 4),
+                    "slots_per_pair": VALU_SLOTS_PER_PAIR}
             sec.append(entry)
             log(f"[bench] {w.name}: {r:.2f} {w.unit} ({100 * r / w.peak:.1f}% of peak)")
             del w

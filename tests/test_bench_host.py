@@ -1,0 +1,107 @@
+"""Host logic of bench.py, on the CPU: the allowed-pair count that every
+TFLOP/s figure divides by, the refusal of more than one GPU, and the
+committed counter summaries being read only while they match the kernel
+source they were taken on."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _brute_pairs(n_q, n_k, causal, window):
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    delta = n_k - n_q
+    ok = np.ones((n_q, n_k), dtype=bool)
+    if causal:
+        ok &= j <= i + delta
+    if window >= 0:
+        ok &= j >= i + delta - window
+    return int(ok.sum())
+
+
+@pytest.mark.parametrize("n_q,n_k,causal,window", [
+    (1, 1, False, -1), (7, 5, True, -1), (5, 7, True, -1), (33, 33, True, 4),
+    (40, 29, False, 3), (29, 40, True, 0), (64, 64, True, 100), (17, 80, False, -1)])
+def test_pairs_match_brute_force(n_q, n_k, causal, window):
+    assert bench.pairs_dense(n_q, n_k, causal, window) == _brute_pairs(n_q, n_k, causal, window)
+
+
+def test_pairs_closed_forms():
+    # non-causal: every pair; causal square: the lower triangle with the diagonal
+    assert bench.pairs_dense(2048, 2048, False, -1) == 2048 * 2048
+    assert bench.pairs_dense(8000, 8000, True, -1) == 8000 * 8001 // 2
+    # causal with W keys left of the diagonal: a triangle of W + 1 rows, then W + 1 per row
+    W = 1024
+    for L in (100, 1025, 1026, 4096):
+        expect = L * (L + 1) // 2 if L <= W + 1 else (W + 1) * (W + 2) // 2 + (W + 1) * (L - W - 1)
+        assert bench.pairs_dense(L, L, True, W) == expect
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def test_traffic_summary_is_read_only_for_its_source(tmp_path):
+    src = tmp_path / "kernel.hip"
+    src.write_text("kernel source v1\n")
+    summary = tmp_path / "traffic.txt"
+    assert bench.read_traffic(str(summary), str(src)) is None  # absent
+    summary.write_text(f"kernel: k\nhbm_bytes_per_launch: 12345\n"
+                       f"kernel_source_sha256: {_sha(src)}\n")
+    assert bench.read_traffic(str(summary), str(src)) == 12345.0
+    src.write_text("kernel source v2\n")
+    assert bench.read_traffic(str(summary), str(src)) is None  # stale
+
+
+def test_mfma_summary_round_trip(tmp_path):
+    """Synthetic counter CSVs in rocprofv3's column layout through
+    mfma_summary, then read back per kernel while the source matches."""
+    src = tmp_path / "kernel.hip"
+    src.write_text("kernel source\n")
+    util_dir, raw_dir = tmp_path / "util", tmp_path / "raw"
+    util_dir.mkdir()
+    raw_dir.mkdir()
+    kname = "void fa::(anonymous namespace)::fwd_bf16_kernel<128, false>(fa::FwdArgs)"
+    other = "void at::native::elementwise_kernel<128, 4>(int)"
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    (util_dir / "a_counter_collection.csv").write_text(
+        head + f'1,"{kname}",MfmaUtil,40.0,0,1000\n2,"{kname}",MfmaUtil,50.0,0,1000\n'
+               f'3,"{kname}",MfmaUtil,60.0,0,1000\n4,"{other}",MfmaUtil,99.0,0,1000\n')
+    rows = []
+    for i, (mops, grbm) in enumerate([(100, 8000), (300, 9000), (200, 10000)]):
+        rows.append(f'{i},"{kname}",SQ_INSTS_VALU_MFMA_MOPS_BF16,{mops},0,{2000 + 1000 * i}')
+        rows.append(f'{i},"{kname}",GRBM_GUI_ACTIVE,{grbm},0,{2000 + 1000 * i}')
+    (raw_dir / "b_counter_collection.csv").write_text(head + "\n".join(rows) + "\n")
+    out = tmp_path / "summary.txt"
+    old = bench.PREFILL_KERNEL_SRC
+    bench.PREFILL_KERNEL_SRC = str(src)
+    try:
+        bench.mfma_summary(str(util_dir), str(raw_dir), "prefill_2k", str(out), "cmd", 1)
+    finally:
+        bench.PREFILL_KERNEL_SRC = old
+    text = out.read_text()
+    assert "kernel: fwd_bf16_kernel<128, false>" in text
+    assert "elementwise" not in text  # only the library's kernels
+    assert "mfma_util_pct: 50.00" in text  # median of 40, 50, 60
+    assert "mfma_flops_bf16: 102400" in text  # median MOPS 200 x 512
+    assert "dispatch_us_under_counters: 3.00" in text  # median of 2, 3, 4 us
+    assert bench.read_mfma_util(str(out), str(src), "fwd_bf16_kernel<128, false>") == 50.0
+    src.write_text("changed\n")
+    assert bench.read_mfma_util(str(out), str(src), "fwd_bf16_kernel<128, false>") is None
