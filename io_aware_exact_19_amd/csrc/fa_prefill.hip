@@ -423,6 +423,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
     vofs[i] = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
   }
   // ring slot of tile g, counted over all items of the workgroup
+  const uint32_t ring_lds = lds_addr(ring);
   auto kslot = [&](int g) { return ring + (g & 3) * 2 * T::kBytes; };
   auto vslot = [&](int g) { return ring + (g & 3) * 2 * T::kBytes + T::kBytes; };
   // queue the DMA of tile j (relative to the item's t_lo) into slot g
@@ -436,13 +437,15 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       it.rv = buffer_rsrc(it.vg + (long long)k0 * rs, nrec);
     }
     const uint32_t base = (uint32_t)(k0 - it.seg0) * row_bytes;
-    char* kdst = kslot(g);
-    char* vdst = vslot(g);
+    // LDS byte address of the slot as an integer (no pointer casts on this
+    // path: a cast of a ring pointer chosen at run time back to the LDS
+    // address space can leave an aperture compare the code generator rejects)
+    const uint32_t kdst = ring_lds + (uint32_t)(g & 3) * 2 * T::kBytes;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
-      const int blk = i * kWaves + wave;
-      dma16(it.rk, base + kofs[i], lds_addr(kdst + blk * 1024));
-      dma16(it.rv, base + vofs[i], lds_addr(vdst + blk * 1024));
+      const uint32_t blk = (uint32_t)(i * kWaves + wave) * 1024;
+      dma16(it.rk, base + kofs[i], kdst + blk);
+      dma16(it.rv, base + vofs[i], kdst + T::kBytes + blk);
     }
   };
   // Q^T operand fragments: lane holds Q[qi][kk*16 + half*8 .. +8]; rows past
@@ -477,6 +480,50 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   }
   int gbase = 0;  // ring index of the current item's tile 0
 
+  // per-row state of an item: the O accumulator u, the reference max m
+  // (base-2 scaled), and this lane-half's partial exp-sums, unrounded (l, for
+  // lse) and over the bf16-rounded probabilities (for O)
+  f32x16_t oacc[D / 32];
+  float m_run, l_run, lr_run;
+  auto init_state = [&]() {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    m_run = kNegInf;
+    l_run = 0.0f;
+    lr_run = 0.0f;
+  };
+  // O = u / l (one division per row, l over the rounded probabilities),
+  // lse = ln 2 * (m + log2 l) (l over the unrounded ones)
+  auto epilogue = [&](uint16_t* og_, int qi_, int n_q_, long long lse_base_) {
+    const float l_tot = sum_halves(l_run);
+    const float lr_tot = sum_halves(lr_run);
+    if (qi_ < n_q_) {
+      const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
+      uint16_t* op = og_ + (long long)qi_ * rs;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + half * 4;
+          u32x2_t pr;
+          pr[0] = pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
+          pr[1] = pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
+          *(u32x2_t*)(op + d) = pr;
+        }
+      if (a.lse != nullptr && half == 0)
+        a.lse[lse_base_ + qi_] = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : kNegInf;
+    }
+  };
+  // Group 1 ends an item half a step after group 0.  Its epilogue is held
+  // over into the next item and run after that item's first landing barrier,
+  // while group 0 computes the first scores (group 1 would wait there
+  // anyway), so group 0 no longer waits for it; the state stays in registers.
+  bool pend = false;
+  uint16_t* p_og = nullptr;
+  int p_qi = 0, p_nq = 0;
+  long long p_lse = 0;
   for (;;) {
   // the item's state is derived again here (its loads were queued earlier;
   // the K/V descriptor window restarts at the first tile queued from here)
@@ -488,18 +535,10 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   const int wq0 = cur.wq0, wq_last = cur.wq_last, w_lo = cur.w_lo, w_hi = cur.w_hi;
   const bool wave_live = cur.wave_live;
   const int qi = wq0 + l32;  // this lane's query row
-  // Q and the first two tiles are in flight together (with the previous
-  // item's output stores); the wait covers all
+  // Q and the first two tiles are in flight together (with group 0's output
+  // stores of the previous item); the wait covers all
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  f32x16_t oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-  float m_run = kNegInf;  // reference max of this row (base-2 scaled)
-  float l_run = 0.0f;     // partial exp-sum over this lane-half's keys (for lse)
-  float lr_run = 0.0f;    // the same over the bf16-rounded probabilities (for O)
 
   // per-lane parts of the LDS operand addresses
   // K rows enter in pi order (see pi_row); sub-block kb adds 32 rows.  The
@@ -721,6 +760,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   if (nt > 0) {
     // steps 0 .. nt: step 0 has no previous tile, step nt no next one
     if (group == 0) {
+      init_state();
       land(0);
       mblock_first(kslot(gbase));
       barrier();
@@ -739,6 +779,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       barrier();  // pairs with group 1's barrier before its last matrix block
     } else {
       land(0);
+      if (pend) epilogue(p_og, p_qi, p_nq, p_lse);
+      pend = false;
+      init_state();
       prefetch(0);
       barrier();
       mblock_first(kslot(gbase));
@@ -756,28 +799,20 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       mblock_last(vslot(gbase + nt - 1));
     }
   } else {
+    if (pend) epilogue(p_og, p_qi, p_nq, p_lse);
+    pend = false;
+    init_state();
     next_loads();
   }
 
-  // epilogue: O = u / l (one division per row, l over the rounded
-  // probabilities), lse = ln 2 * (m + log2 l) (l over the unrounded ones)
-  const float l_tot = sum_halves(l_run);
-  const float lr_tot = sum_halves(lr_run);
-  if (qi < n_q) {
-    const float inv = lr_tot > 0.0f ? 1.0f / lr_tot : 0.0f;
-    uint16_t* op = og + (long long)qi * rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + g4 * 8 + half * 4;
-        u32x2_t pr;
-        pr[0] = pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv);
-        pr[1] = pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv);
-        *(u32x2_t*)(op + d) = pr;
-      }
-    if (a.lse != nullptr && half == 0)
-      a.lse[cur.lse_base + qi] = l_tot > 0.0f ? (m_run + log2_hw(l_tot)) * kLn2 : kNegInf;
+  if (group == 1 && has_next) {
+    pend = true;
+    p_og = og;
+    p_qi = qi;
+    p_nq = n_q;
+    p_lse = cur.lse_base;
+  } else {
+    epilogue(og, qi, n_q, cur.lse_base);
   }
   if (!has_next) break;
   gbase += nt;
