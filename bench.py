@@ -78,9 +78,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _local_includes(path, seen):
+    """``path`` and every header it pulls in with #include "..." from its own
+    directory, depth first, each once."""
+    path = os.path.abspath(path)
+    if path in seen or not os.path.exists(path):
+        return
+    seen.append(path)
+    with open(path) as f:
+        for line in f:
+            t = line.strip()
+            if t.startswith("#include") and '"' in t:
+                _local_includes(os.path.join(os.path.dirname(path), t.split('"')[1]), seen)
+
+
 def sha256(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Digest of a kernel source together with the local headers it includes
+    (a change to a shared helper changes the compiled kernel too)."""
+    files = []
+    _local_includes(path, files)
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def pairs_dense(n_q, n_k, causal, window):

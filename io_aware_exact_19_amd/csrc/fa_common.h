@@ -54,11 +54,14 @@ __device__ __forceinline__ bf16x8_t to_bf16x8(float a0, float a1, float a2, floa
   return r;
 }
 
+// two floats to bf16 (round to nearest even), lo in the low half: one
+// packed conversion (a union of two scalars compiles to two conversions,
+// a shift and an or)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  union { __bf16 b[2]; uint32_t u; } p;
-  p.b[0] = (__bf16)lo;
-  p.b[1] = (__bf16)hi;
-  return p.u;
+  __bf16 __attribute__((ext_vector_type(2))) r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

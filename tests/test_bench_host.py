@@ -105,3 +105,17 @@ def test_mfma_summary_round_trip(tmp_path):
     assert bench.read_mfma_util(str(out), str(src), "fwd_bf16_kernel<128, false>") == 50.0
     src.write_text("changed\n")
     assert bench.read_mfma_util(str(out), str(src), "fwd_bf16_kernel<128, false>") is None
+
+
+def test_source_digest_covers_included_headers(tmp_path):
+    """A kernel's digest changes when a local header it includes changes,
+    and not when an unrelated file does."""
+    (tmp_path / "common.h").write_text("inline int f() { return 1; }\n")
+    (tmp_path / "other.h").write_text("unrelated\n")
+    src = tmp_path / "kernel.hip"
+    src.write_text('#include "common.h"\n#include <hip/hip_runtime.h>\nint g();\n')
+    d0 = bench.sha256(str(src))
+    (tmp_path / "other.h").write_text("changed\n")
+    assert bench.sha256(str(src)) == d0
+    (tmp_path / "common.h").write_text("inline int f() { return 2; }\n")
+    assert bench.sha256(str(src)) != d0
