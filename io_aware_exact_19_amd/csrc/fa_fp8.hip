@@ -258,15 +258,17 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
       int hi = n_k - 1, lo = 0;
       if (causal) hi = min(hi, qi + delta);
       if (W >= 0) lo = max(lo, qi + delta - W);
-      const int e = k0 + 32 * half - lo, f = hi - k0 - 32 * half;
+      // key kj = k0 + 32 half + j is allowed iff 0 <= kj - lo <= hi - lo: one
+      // unsigned compare per key (kj < lo wraps to a large value); a row
+      // with hi < lo allows none
+      const int span = hi - lo;
+      const uint32_t e = span < 0 ? 0x80000000u : (uint32_t)(k0 + 32 * half - lo);
+      const uint32_t range = span < 0 ? 0u : (uint32_t)span;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = 16 * kb + r;
-          const uint32_t bad = (uint32_t)(((e + j) | (f - j)) >> 31);
-          s[kb][r] = __uint_as_float((bad & 0xff800000u) | (~bad & __float_as_uint(s[kb][r])));
-        }
+        for (int r = 0; r < 16; ++r)
+          if (e + (uint32_t)(16 * kb + r) > range) s[kb][r] = kNegInf;
     }
     float p[2][16];
 #pragma unroll

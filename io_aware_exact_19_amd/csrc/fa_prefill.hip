@@ -973,19 +973,22 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
                            (W >= 0 && k0 < wq_last + delta - W);
     if (need_mask) {
       // allowed keys of this lane's row: [lo, hi]; key kj = k0 + 8 half + c
-      // is allowed iff (kj - lo) and (hi - kj) are both >= 0: their sign bits
-      // make a select mask (no compare results in scalar registers)
+      // is allowed iff 0 <= kj - lo <= hi - lo, one unsigned compare per key
+      // (kj < lo wraps to a large value); a row with hi < lo allows none.
+      // Three vector instructions per key against five for two sign tests;
+      // this kernel has the scalar registers the compare results take.
       int hi = n_k - 1, lo = 0;
       if (causal) hi = min(hi, qi + delta);
       if (W >= 0) lo = max(lo, qi + delta - W);
-      const int e = k0 + 8 * half - lo, f = hi - k0 - 8 * half;
+      const int span = hi - lo;
+      const uint32_t e = span < 0 ? 0x80000000u : (uint32_t)(k0 + 8 * half - lo);
+      const uint32_t range = span < 0 ? 0u : (uint32_t)span;
 #pragma unroll
       for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
-          const uint32_t bad = (uint32_t)(((e + c) | (f - c)) >> 31);
-          sacc[kb][r] = __uint_as_float((bad & 0xff800000u) | (~bad & __float_as_uint(sacc[kb][r])));
+          const uint32_t c = kb * 32 + 16 * (r >> 3) + (r & 7);
+          if (e + c > range) sacc[kb][r] = kNegInf;
         }
     }
 
