@@ -672,21 +672,28 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
     const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
                            (W >= 0 && k0 < wq_last + delta - W);
     if (need_mask) {
-      // allowed keys of this lane's row: [lo, hi]; with e = key - lo - 8 half,
-      // a key is allowed iff both (e + c) and (hi - lo - 8 half - c) are >= 0,
-      // c being the key's constant offset in the tile; the sign bits of the
-      // two make a select mask for v_bfi (no compare results in SGPRs)
+      // allowed keys of this lane's row: [lo, hi]; key kj = k0 + 8 half + c
+      // is allowed iff 0 <= kj - lo <= hi - lo, one unsigned compare per key
+      // (kj < lo wraps to a large value; a row with hi < lo allows none).
+      // Compare and select go through VCC one key at a time: left to the
+      // compiler, the 32 compares each take a scalar register pair, which
+      // this kernel does not have to spare
       int hi = n_k - 1, lo = 0;
       if (causal) hi = min(hi, qi + delta);
       if (W >= 0) lo = max(lo, qi + delta - W);
-      const int e = k0 + 8 * half - lo, f = hi - k0 - 8 * half;
+      const int span = hi - lo;
+      const uint32_t e = span < 0 ? 0x80000000u : (uint32_t)(k0 + 8 * half - lo);
+      const uint32_t range = span < 0 ? 0u : (uint32_t)span;
+      const float ninf = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
-          const uint32_t bad = (uint32_t)(((e + c) | (f - c)) >> 31);
-          sacc[kb][r] = __uint_as_float((bad & 0xff800000u) | (~bad & __float_as_uint(sacc[kb][r])));
+          const uint32_t t = e + (uint32_t)(kb * 32 + 16 * (r >> 3) + (r & 7));
+          float x = sacc[kb][r];
+          asm("v_cmp_lt_u32 vcc, %1, %2\n\tv_cndmask_b32 %0, %0, %3, vcc"
+              : "+v"(x) : "v"(range), "v"(t), "v"(ninf) : "vcc");
+          sacc[kb][r] = x;
         }
     }
     // Probabilities against the current reference max, accepted when this
