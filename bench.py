@@ -56,6 +56,7 @@ PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 PEAK_FP32_TFLOPS = 157.3    # dense fp32 matrix-core peak
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0     # engine clock the published matrix-core peaks assume
 # vector issue: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz, in lane
 # issue slots per second (no packed fp32 arithmetic is used)
 PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -287,6 +288,112 @@ def make_fp8(torch, fa, inputs, configs, cfg, causal=False):
     return w
 
 
+# ---------------------------------------------------------------- clock
+
+
+class ClockSampler:
+    """Engine (graphics) clock of the GPU that torch's device 0 is, from the
+    GPU metrics table that amdsmi reads: the per-XCD current clocks averaged
+    over the XCDs, and the socket power.  The firmware refreshes that table
+    only every few hundred milliseconds, so a background thread polls it and
+    keeps each distinct table taken while the graphics engine was busy
+    (average activity >= 80 %).  Read-only queries; any failure leaves the
+    snapshots empty and names the reason."""
+
+    def __init__(self, torch, period_s=0.02):
+        import threading
+
+        self.period_s = period_s
+        self.snapshots = []        # (MHz averaged over the XCDs, socket W)
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+
+            self._amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            props = torch.cuda.get_device_properties(0)
+            want = (int(getattr(props, "pci_domain_id", 0)), int(getattr(props, "pci_bus_id", -1)))
+            for h in handles:
+                dom, bus = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[:2]
+                if (int(dom, 16), int(bus, 16)) == want:
+                    self._h = h
+            if self._h is None and len(handles) == 1:
+                self._h = handles[0]
+            if self._h is None:
+                self.error = f"no amdsmi device with PCI domain/bus {want}"
+        except Exception as e:  # noqa: BLE001 - report, never fail the bench
+            self.error = f"amdsmi unavailable: {e}"
+
+    @staticmethod
+    def _num(x):
+        return float(x) if isinstance(x, (int, float)) else None
+
+    def _read(self):
+        """(key identifying the table, MHz, W) or None when the table was not
+        taken under load."""
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        act = self._num(m.get("average_gfx_activity"))
+        if act is None or act < 80:
+            return None
+        xs = m.get("current_gfxclks")
+        xs = [float(x) for x in xs if isinstance(x, (int, float)) and x > 0] \
+            if isinstance(xs, list) else []
+        mhz = sum(xs) / len(xs) if xs else self._num(m.get("current_gfxclk"))
+        if mhz is None:
+            return None
+        key = (m.get("gfx_activity_acc"), tuple(xs), m.get("current_socket_power"))
+        return key, mhz, self._num(m.get("current_socket_power"))
+
+    def _run(self):
+        seen = set()
+        while not self._stop.is_set():
+            try:
+                r = self._read()
+            except Exception as e:  # noqa: BLE001
+                self.error = f"metrics read failed: {e}"
+                return
+            if r is not None and r[0] not in seen:
+                seen.add(r[0])
+                self.snapshots.append((r[1], r[2]))
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+
+        if self._h is None:
+            return self
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        """Stop; returns (median MHz, median W, number of snapshots) or
+        (None, None, 0)."""
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=2.0)
+        if not self.snapshots:
+            if self.error is None:
+                self.error = "no metrics table taken under load"
+            return None, None, 0
+        mhz = statistics.median(x for x, _ in self.snapshots)
+        ws = [w for _, w in self.snapshots if w is not None]
+        return mhz, (statistics.median(ws) if ws else None), len(self.snapshots)
+
+
+def measure_clock(torch, w, seconds):
+    """Run ``w`` back to back for ``seconds`` while the clock sampler polls;
+    returns (MHz, W, snapshots, error)."""
+    clock = ClockSampler(torch).start()
+    settle(torch, w, seconds * 1e3)
+    mhz, watts, n = clock.stop()
+    return mhz, watts, n, clock.error
+
+
 # ---------------------------------------------------------------- timing
 
 
@@ -394,27 +501,97 @@ def read_traffic(summary, src):
 
 
 def cpu_baseline(cfg):
-    """The fp64 oracle, as it stands, on every (batch, head) slice of the
-    headline workload, timed on this host."""
-    import numpy as np
+    """The fp64 oracle, as it stands, timed on this host: every (batch, head)
+    slice of the headline workload (the ``value``), then a bounded sample of
+    each of the other workloads (``per_workload``), each rate against the same
+    algorithmic work as the GPU figure (FLOPs of allowed pairs; for decode,
+    the K/V bytes of the valid cache rows).  Inputs are generated outside the
+    timed calls."""
+    import torch
     from threadpoolctl import threadpool_info
 
     import oracle
     from io_aware_exact_19_amd import configs, inputs
 
+    def f64(t):
+        return t.float().double().numpy()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
     B, H, N, d = cfg["batch"], cfg["heads"], cfg["seqlen"], cfg["d"]
-    q, k, v = inputs.dense_qkv(B, N, N, H, d, cfg["seed"])
-    qn, kn, vn = (x.float().double().numpy() for x in (q, k, v))
-    t0 = time.perf_counter()
-    oracle.attention_dense(qn, kn, vn, configs.default_scale(d), False, -1)
-    dt = time.perf_counter() - t0
+    q, k, v = (f64(x) for x in inputs.dense_qkv(B, N, N, H, d, cfg["seed"]))
+    sc = configs.default_scale(d)
+    dt = timed(lambda: oracle.attention_dense(q, k, v, sc, False, -1))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     flops = 4 * d * H * B * N * N
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
-                sample=f"all {B * H} (batch, head) slices of the B{B} H{H} N{N} d{d} non-causal "
-                       f"workload once: {dt:.2f} s, fp64, score matrix materialised",
-                seconds=round(dt, 3), host_cpus=len(os.sched_getaffinity(0)))
+    out = dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+               sample=f"all {B * H} (batch, head) slices of the B{B} H{H} N{N} d{d} non-causal "
+                      f"workload once: {dt:.2f} s, fp64, score matrix materialised",
+               seconds=round(dt, 3), host_cpus=len(os.sched_getaffinity(0)))
+
+    per = []
+
+    def add(workload, sample, seconds, work, unit):
+        scale = 1e9
+        per.append(dict(workload=workload, sample=sample, seconds=round(seconds, 3),
+                        value=round(work / seconds / scale, 3), unit=unit))
+        log(f"[bench] oracle {workload}: {seconds:.2f} s, {work / seconds / scale:.2f} {unit}")
+
+    # small fp32 workload, whole
+    c = configs.SMALL_FP32
+    n, hh, dd = c["seqlen"], c["heads"], c["d"]
+    qs, ks, vs = (x.double().numpy()
+                  for x in inputs.dense_qkv(c["batch"], n, n, hh, dd, c["seed"], torch.float32))
+    t = timed(lambda: oracle.attention_dense(qs, ks, vs, configs.default_scale(dd), False, -1))
+    add(c["name"], "whole workload", t, 4 * dd * hh * c["batch"] * n * n, "GFLOP/s")
+
+    # headline shape, causal: every slice (the oracle masks the full matrix)
+    t = timed(lambda: oracle.attention_dense(q, k, v, sc, True, -1))
+    add(cfg["name"] + "_causal", f"all {B * H} slices", t,
+        4 * d * H * B * pairs_dense(N, N, True, -1), "GFLOP/s")
+    del q, k, v
+
+    # 8000-token causal prompt: one head of 32
+    c = configs.LONG_8K
+    n, dd = c["seqlen"], c["d"]
+    ql, kl, vl = (f64(x[:, :, :1]) for x in inputs.dense_qkv(1, n, n, 1, dd, c["seed"]))
+    t = timed(lambda: oracle.attention_dense(ql, kl, vl, configs.default_scale(dd), True, -1))
+    add(c["name"], f"head 0 of {c['heads']}", t, 4 * dd * pairs_dense(n, n, True, -1), "GFLOP/s")
+    del ql, kl, vl
+
+    # packed batch: one head of 16, every sequence
+    c = configs.VARLEN
+    lens = inputs.lengths(c["nseq"], c["len_lo"], c["len_hi"], c["seed"])
+    cu = inputs.cu_seqlens(lens).numpy()
+    qv, kv, vv = (f64(x[:, :1]) for x in inputs.varlen_qkv(lens, 1, c["d"], c["seed"]))
+    t = timed(lambda: oracle.attention_varlen(qv, kv, vv, cu, cu, configs.default_scale(c["d"]),
+                                              True, c["window_left"]))
+    pairs = sum(pairs_dense(int(x), int(x), True, c["window_left"]) for x in lens)
+    add(c["name"], f"head 0 of {c['heads']}, all {c['nseq']} sequences", t, 4 * c["d"] * pairs,
+        "GFLOP/s")
+    del qv, kv, vv
+
+    # decode: all heads of the 8 first sequences (their valid cache rows drawn
+    # on the host: same shapes and distribution as the GPU workload)
+    c = configs.DECODE
+    lens = inputs.lengths(c["batch"], c["len_lo"], c["len_hi"], c["seed"])[:8]
+    hh, dd = c["heads"], c["d"]
+    qd = f64(inputs.normal((8, 1, hh, dd), inputs.subseed(c["seed"], "q")))
+    tot, byts = 0.0, 0
+    for b in range(8):
+        nb = int(lens[b])
+        kc = f64(inputs.normal((1, nb, hh, dd), inputs.subseed(c["seed"], "k", b)))
+        vc = f64(inputs.normal((1, nb, hh, dd), inputs.subseed(c["seed"], "v", b)))
+        tot += timed(lambda: oracle.attention_decode(qd[b:b + 1], kc, vc, [nb],
+                                                     configs.default_scale(dd)))
+        byts += nb * hh * dd * 2 * 2
+    add(c["name"], f"all {hh} heads of 8 of {c['batch']} sequences", tot, byts, "GB/s")
+    out["per_workload"] = per
+    return out
 
 
 # ----------------------------------------------------- counter summaries
@@ -580,6 +757,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="back-to-back launches before the warmup steps (engine clock ramp)")
+    ap.add_argument("--clock-s", type=float, default=2.5,
+                    help="seconds of back-to-back headline launches while the clock is sampled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-target", default=None,
@@ -663,6 +842,11 @@ def main():
         f"steps {args.steps}")
     wall_ms, mean_ms, chunks = time_launches(torch, head, args.steps, args.warmup, args.settle_ms)
     achieved = rate(head, mean_ms)
+    # the engine clock while the same launches run back to back (right after
+    # the timed region, same inputs): the firmware's metrics table refreshes
+    # only every few hundred milliseconds, too rarely to sample the timed
+    # launches themselves
+    clock_mhz, clock_w, clock_n, clock_err = measure_clock(torch, head, args.clock_s)
     evicted_ms = time_evicted(torch, head)
     traffic = read_traffic(TRAFFIC_SUMMARY, PREFILL_KERNEL_SRC)
     result = {
@@ -693,8 +877,25 @@ def main():
             "mean_launch_ms": round(mean_ms, 5),
             "chunk_ms_range": chunks,
             "median_launch_ms_cache_evicted": round(evicted_ms, 5),
+            # the published peak assumes the 2.4 GHz maximum engine clock;
+            # the same fraction against the peak at the clock measured while
+            # this kernel ran back to back
+            "clock_mhz": round(clock_mhz, 1) if clock_mhz else None,
+            "clock_snapshots": clock_n,
+            "socket_power_w": clock_w,
+            "clock_source": (f"amdsmi GPU metrics table: current gfx clock averaged over the "
+                             f"XCDs, median of the distinct tables taken under load during "
+                             f"{args.clock_s:.1f} s of back-to-back launches after the timed "
+                             f"region" if clock_mhz else clock_err),
+            "peak_at_measured_clock": (round(PEAK_BF16_TFLOPS * clock_mhz / PEAK_CLOCK_MHZ, 1)
+                                       if clock_mhz else None),
+            "frac_at_measured_clock": (round(achieved / (PEAK_BF16_TFLOPS * clock_mhz /
+                                                         PEAK_CLOCK_MHZ), 4)
+                                       if clock_mhz else None),
         },
     }
+    if clock_mhz:
+        log(f"[bench] engine clock {clock_mhz:.0f} MHz, {clock_w} W ({clock_n} metrics tables)")
     log(f"[bench] {head.name}: {result['value']} TFLOP/s wall, kernel {achieved:.1f} TFLOP/s")
     del head
     torch.cuda.empty_cache()
@@ -733,7 +934,7 @@ def main():
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on the headline workload")
+        log("[bench] timing the CPU oracle (headline workload, then a sample of each other one)")
         result["cpu_baseline"] = cpu_baseline(configs.PREFILL_2K)
 
     print(json.dumps(result), flush=True)

@@ -34,7 +34,9 @@
  *                     (bottom-right aligned);
  *      window_left W: key j allowed iff j >= i + delta - W  (W < 0: none);
  *    with both, a row sees at most W + 1 keys.  A row with no allowed key
- *    gets O = 0 and lse = -inf.
+ *    gets O = 0 and lse = -inf.  W >= seqlen_k admits every key and is
+ *    treated as no window.
+ *  - Head dim d must be 64 or 128 (FA_ERR_INVALID_ARG otherwise).
  *  - Arithmetic: bf16 inputs are multiplied on matrix cores with fp32
  *    accumulation; the softmax runs in fp32 in base 2 with log2(e) folded into
  *    the scale; the probabilities are rounded to bf16 (RNE) before the P V
@@ -51,9 +53,11 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad flag, scale not finite > 0 */
-  FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: head dim, chunk size, varlen+fp32,
-                              a grid over 2^31 workgroups, a key row (heads*d) over 64 MiB */
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, head dim d other than
+                              64 or 128, bad flag, scale not finite > 0 */
+  FA_ERR_UNSUPPORTED = -2, /* well-formed but not built: decode chunk size, varlen+fp32,
+                              fp8 at d = 64, a grid over 2^31 workgroups, a key row (heads*d)
+                              over 64 MiB */
   FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
   FA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
 } fa_status;
@@ -191,8 +195,8 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
  * the P V product, O divided by the sum of exactly those rounded
  * probabilities (so each output row is a convex combination of V rows),
  * lse from the unrounded sum.
- * No workspace.  FA_ERR_UNSUPPORTED for d != 128 or when 64 rows of
- * heads * d bytes reach 4 GiB.
+ * No workspace.  FA_ERR_UNSUPPORTED for d = 64 (valid, not built here) or
+ * when 64 rows of heads * d bytes reach 4 GiB.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* descale_q, const float* descale_k, const float* descale_v, int batch,

@@ -167,6 +167,11 @@ def _check_tensor(name, t, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_workspace(ws):
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU")
+
+
 def attention(q, k, v, *, scale=None, causal=False, window_left=-1, return_lse=True, out=None,
               lse_out=None, stream=None):
     """Dense attention: q [B, n_q, H, d], k/v [B, n_k, H, d], bf16 or fp32.
@@ -188,6 +193,8 @@ def attention(q, k, v, *, scale=None, causal=False, window_left=-1, return_lse=T
     if return_lse:
         lse = torch.empty((B, H, n_q), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
         _check_tensor("lse", lse, torch.float32, 3)
+        if tuple(lse.shape) != (B, H, n_q):
+            raise ValueError(f"lse_out must be [B, H, n_q] = {(B, H, n_q)}, got {tuple(lse.shape)}")
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     fn = fa_fwd if dtype == torch.bfloat16 else fa_fwd_fp32
     st = fn(q, k, v, o, lse, B, H, n_q, n_k, d, s, int(causal), int(window_left), None, None,
@@ -236,6 +243,9 @@ def attention_kvcache(q, k_cache, v_cache, seqlens_k, *, scale=None, causal=True
     if v_cache.shape != k_cache.shape or seqlens_k.numel() != B:
         raise ValueError("cache/seqlens shape mismatch")
     o = torch.empty_like(q) if out is None else out
+    _check_tensor("out", o, torch.bfloat16, 4)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
     lse = torch.empty((B, H, n_new), dtype=torch.float32, device=q.device) if return_lse else None
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = fa_fwd_kvcache(q, k_cache, v_cache, seqlens_k, o, lse, B, H, n_new, k_cache.shape[1], d,
@@ -263,6 +273,7 @@ def attention_backward(q, k, v, o, lse, dout, *, scale=None, causal=False, windo
     need = fa_bwd_workspace_size(B, H, n_q)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, n_q, n_k, d, s, int(causal),
                 int(window_left), workspace, workspace.numel() * workspace.element_size(), stream)
@@ -290,7 +301,11 @@ def decode(q, k_cache, v_cache, seqlens_k, *, scale=None, chunk=256, workspace=N
     need = fa_decode_workspace_size(B, H, max_len, d, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     o = torch.empty_like(q) if out is None else out
+    _check_tensor("out", o, torch.bfloat16, 4)
+    if o.shape != q.shape:
+        raise ValueError("out must have q's shape")
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
     s = 1.0 / math.sqrt(d) if scale is None else float(scale)
     st = fa_decode(q, k_cache, v_cache, seqlens_k, o, lse, B, H, max_len, d, s, chunk,

@@ -11,16 +11,27 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Head dims the operation is defined for here: 64 and 128.  Any other value
+// is an invalid argument, not a missing build.
+bool head_dim_valid(int d) { return d == 64 || d == 128; }
+
+// A left window of seqlen_k or more keys admits every key of every row (the
+// bound i + delta - W is then <= n_k - 1 - W < 0 for every row i), so it is
+// the same as no window.  Mapping it to -1 here keeps the kernels' int32
+// bound q0 + delta - W from overflowing for W near INT_MAX.
+int effective_window(int window_left, int seqlen_k) {
+  return window_left < 0 || window_left >= seqlen_k ? -1 : window_left;
+}
+
 int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, float* lse,
                int batch, int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
                int window_left, const int* cu_q, const int* cu_k, void* stream,
                const int* seqlens_k = nullptr) {
   if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
-  if (d <= 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_valid(d)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if ((cu_q == nullptr) != (cu_k == nullptr)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (fp32 && cu_q != nullptr) return FA_ERR_UNSUPPORTED;
   if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;  // nothing to compute
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
@@ -55,7 +66,7 @@ int fwd_common(bool fp32, const void* q, const void* k, const void* v, void* o, 
   a.seqlen_k = seqlen_k;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal;
-  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_left = effective_window(window_left, seqlen_k);
   a.cu_q = cu_q;
   a.cu_k = cu_k;
   a.seqlens_k = seqlens_k;
@@ -104,10 +115,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int seqlen_q,
            int seqlen_k, int d, float scale, int causal, int window_left, void* workspace,
            size_t workspace_bytes, void* stream) {
-  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_valid(d)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (batch == 0 || heads == 0 || (seqlen_q == 0 && seqlen_k == 0)) return FA_OK;
   const bool rows = seqlen_q > 0, keys = seqlen_k > 0;
   if (rows && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr || dq == nullptr))
@@ -147,7 +158,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal;
-  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_left = effective_window(window_left, seqlen_k);
   const hipError_t e = fa::launch_bwd(a, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -162,9 +173,9 @@ size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int ch
 int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
               void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
               int chunk, void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 0 || heads < 0 || max_len < 0 || d <= 0 || chunk <= 0) return FA_ERR_INVALID_ARG;
+  if (batch < 0 || heads < 0 || max_len < 0 || chunk <= 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_valid(d)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (chunk != 64 && chunk != 128 && chunk != 256 && chunk != 512) return FA_ERR_UNSUPPORTED;
   if (batch == 0 || heads == 0) return FA_OK;
   if (max_len == 0) return FA_ERR_INVALID_ARG;
@@ -206,10 +217,11 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* descale_q, const float* descale_k, const float* descale_v, int batch,
                int heads, int seqlen_q, int seqlen_k, int d, float scale, int causal,
                int window_left, void* stream) {
-  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (batch < 0 || heads < 0 || seqlen_q < 0 || seqlen_k < 0) return FA_ERR_INVALID_ARG;
+  if (!head_dim_valid(d)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 128) return FA_ERR_UNSUPPORTED;  // d = 64 is valid but has no fp8 kernel
   if (batch == 0 || heads == 0 || seqlen_q == 0) return FA_OK;
   if (q == nullptr || o == nullptr || descale_q == nullptr || descale_k == nullptr ||
       descale_v == nullptr)
@@ -240,7 +252,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   a.seqlen_k = seqlen_k;
   a.scale = scale;
   a.causal = causal;
-  a.window_left = window_left;
+  a.window_left = effective_window(window_left, seqlen_k);
   const hipError_t e = fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -72,6 +72,17 @@ def varlen_qkv(lens, heads, d, seed, dtype=torch.bfloat16):
     return q, k, v
 
 
+def varlen_qkv_pair(lens_q, lens_k, heads, d, seed, dtype=torch.bfloat16):
+    """Packed Q [sum(lens_q), H, d] and K/V [sum(lens_k), H, d]: sequence i
+    has lens_q[i] queries and lens_k[i] keys (cross-length packing)."""
+    tq = int(torch.as_tensor(lens_q).sum())
+    tk = int(torch.as_tensor(lens_k).sum())
+    q = normal((tq, heads, d), subseed(seed, "q"), dtype)
+    k = normal((tk, heads, d), subseed(seed, "k"), dtype)
+    v = normal((tk, heads, d), subseed(seed, "v"), dtype)
+    return q, k, v
+
+
 def decode_cache(batch, max_len, heads, d, seqlens, seed, device, name, dtype=torch.bfloat16,
                  pad=float("nan")):
     """KV cache [B, max_len, H, d]: sequence b's first seqlens[b] rows drawn

@@ -71,8 +71,9 @@ def _fwd(fn=fa.fa_fwd, **kw):
     (dict(seqlen_q=-1), fa.FA_ERR_INVALID_ARG),
     (dict(seqlen_k=-5), fa.FA_ERR_INVALID_ARG),
     (dict(d=0), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_INVALID_ARG),
+    (dict(d=-64), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(scale=-0.1), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
@@ -117,7 +118,8 @@ def _dec(**kw):
     (dict(k_cache=P + 4), fa.FA_ERR_INVALID_ARG),
     (dict(batch=-1), fa.FA_ERR_INVALID_ARG),
     (dict(max_len=0), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_INVALID_ARG),
     (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
     (dict(chunk=0), fa.FA_ERR_INVALID_ARG),
     # one 512-key chunk of 16384 heads x 128 dims spans 2 GiB of cache rows
@@ -146,7 +148,7 @@ def _kvc(**kw):
     (dict(max_len=0), fa.FA_ERR_INVALID_ARG),
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
     (dict(batch=0), fa.FA_OK),
     (dict(seqlen_q=0), fa.FA_OK),
 ])
@@ -171,7 +173,8 @@ def _bwd(**kw):
     (dict(lse=P + 2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),
-    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
     (dict(workspace_bytes=2 * 2 * 4 * 64 * 4 - 1), fa.FA_ERR_WORKSPACE),
     (dict(batch=0), fa.FA_OK),
 ])
@@ -233,7 +236,8 @@ def _fp8(**kw):
     (dict(lse=P + 1), fa.FA_ERR_INVALID_ARG),
     (dict(batch=-1), fa.FA_ERR_INVALID_ARG),
     (dict(seqlen_k=-1), fa.FA_ERR_INVALID_ARG),
-    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),   # valid head dim, no fp8 kernel for it
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),

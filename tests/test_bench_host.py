@@ -119,3 +119,64 @@ def test_source_digest_covers_included_headers(tmp_path):
     assert bench.sha256(str(src)) == d0
     (tmp_path / "common.h").write_text("inline int f() { return 2; }\n")
     assert bench.sha256(str(src)) != d0
+
+
+class _FakeSmi:
+    """Stands in for amdsmi: a metrics table that changes every third read,
+    idle for the first two tables."""
+
+    class AmdSmiClkType:
+        GFX = 0
+
+    def __init__(self):
+        self.reads = 0
+
+    def amdsmi_init(self):
+        pass
+
+    def amdsmi_get_processor_handles(self):
+        return ["h0"]
+
+    def amdsmi_get_gpu_device_bdf(self, h):
+        return "0000:0a:00.0"
+
+    def amdsmi_get_gpu_metrics_info(self, h):
+        self.reads += 1
+        t = (self.reads - 1) // 3
+        busy = t >= 2
+        return {"average_gfx_activity": 94 if busy else 0,
+                "gfx_activity_acc": 1000 + t,
+                "current_socket_power": 1200 + t if busy else 240,
+                "current_gfxclks": [1800 + t, 1700 + t, "N/A"] if busy else [95, 96]}
+
+
+def test_clock_sampler_keeps_distinct_loaded_tables(monkeypatch):
+    import types
+
+    fake = _FakeSmi()
+    mod = types.ModuleType("amdsmi")
+    for name in dir(fake):
+        if name.startswith("amdsmi_") or name == "AmdSmiClkType":
+            setattr(mod, name, getattr(fake, name))
+    monkeypatch.setitem(sys.modules, "amdsmi", mod)
+
+    class _Props:
+        pci_domain_id, pci_bus_id = 0, 10
+
+    class _Cuda:
+        @staticmethod
+        def get_device_properties(i):
+            return _Props()
+
+    class _Torch:
+        cuda = _Cuda
+
+    c = bench.ClockSampler(_Torch, period_s=0.0)
+    assert c.error is None
+    reads = [c._read() for _ in range(12)]
+    # idle tables (the first 6 reads) are dropped; each loaded table is the
+    # XCD mean of its numeric clocks
+    assert reads[:6] == [None] * 6
+    assert reads[6][1] == (1802 + 1702) / 2 and reads[6][2] == 1202
+    keys = {r[0] for r in reads[6:]}
+    assert len(keys) == 2  # tables 2 and 3, three reads each

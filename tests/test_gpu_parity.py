@@ -3,9 +3,9 @@ oracle on the same seeded inputs, element by element.
 
 Small shapes span several 128-row query tiles and 64-key K/V tiles with
 ragged tails; the five workloads run at full size in the launch configuration
-the bench times, checked on every output (2k prefill), on sampled rows of
-every head (8000-token prompt), on sampled heads of every sequence (packed
-batch) and on sampled (sequence, head) pairs (decode).
+the bench times, checked on every output (2k prefill, packed batch), on every
+row of four heads and sampled rows of the others (8000-token prompt) and on
+every head of ten sequences (decode).
 """
 
 import math
@@ -144,7 +144,8 @@ def test_workload_prefill_2k(causal, q_mult):
 
 def test_workload_long_8k():
     """B1 H32 N8000 causal d128: sampled rows (every tile boundary near the
-    start, the middle and the 64-row tail tile) of every head."""
+    start, the middle and the 64-row tail tile) of every head, and every row
+    of four heads."""
     c = configs.LONG_8K
     N, H, d = c["seqlen"], c["heads"], c["d"]
     q, k, v = inputs.dense_qkv(1, N, N, H, d, c["seed"])
@@ -164,6 +165,10 @@ def test_workload_long_8k():
         o_ref[:, h], lse_ref[h] = oracle.sdpa(qn[0, rows, h], kn[0, :, h], vn[0, :, h], s, True,
                                              q_index=rows, n_q=N)
     check(o[0, rows], lse[0][:, rows], o_ref, lse_ref, torch.bfloat16, "long 8k sampled rows")
+    # every row of four heads (first, last and two inside, on different XCDs)
+    for h in (0, 11, 22, 31):
+        o_h, lse_h = oracle.sdpa(qn[0, :, h], kn[0, :, h], vn[0, :, h], s, True)
+        check(o[0, :, h], lse[0, h], o_h, lse_h, torch.bfloat16, f"long 8k head {h}, all rows")
 
 
 def _varlen_case(lens, H, d, causal, W, seed, heads_checked=None):
@@ -302,11 +307,10 @@ def test_varlen_equals_per_sequence_dense():
 
 def test_workload_varlen():
     """16 sequences, lengths U[128, 4096], H16 d64, causal + window 1024;
-    two heads checked on every row of every sequence."""
+    every head checked on every row of every sequence."""
     c = configs.VARLEN
     lens = inputs.lengths(c["nseq"], c["len_lo"], c["len_hi"], c["seed"])
-    _varlen_case(lens, c["heads"], c["d"], c["causal"], c["window_left"], c["seed"],
-                 heads_checked=[0, 11])
+    _varlen_case(lens, c["heads"], c["d"], c["causal"], c["window_left"], c["seed"])
 
 
 def _decode_case(B, H, max_len, d, lens, chunk, seed, pairs=None):
@@ -327,11 +331,14 @@ def _decode_case(B, H, max_len, d, lens, chunk, seed, pairs=None):
     got_o = torch.zeros((len(pairs), d), dtype=torch.bfloat16)
     got_l = torch.zeros(len(pairs))
     qn = _np(q.cpu())
+    rows_of = {}
     for i, (b, h) in enumerate(pairs):
         n = int(lens[b])
-        kn = _np(kc[b, :n, h].cpu())
-        vn = _np(vc[b, :n, h].cpu())
-        ob, lb = oracle.sdpa(qn[b, :, h], kn, vn, s)
+        if b not in rows_of:  # one host copy of a sequence's valid rows, all heads
+            rows_of.clear()
+            rows_of[b] = (kc[b, :n].cpu(), vc[b, :n].cpu())
+        kb, vb = rows_of[b]
+        ob, lb = oracle.sdpa(qn[b, :, h], _np(kb[:, h]), _np(vb[:, h]), s)
         o_ref[i], lse_ref[i] = ob[0], lb[0]
         got_o[i], got_l[i] = o[b, 0, h], lse[b, h]
     check(got_o, got_l, o_ref, lse_ref, torch.bfloat16, what)
@@ -481,11 +488,121 @@ def test_workload_kvcache():
 
 def test_workload_decode():
     """B64 H32, lengths U[1024, 32768], d128, 256-key chunks, full-size NaN
-    padded caches; 8 sequences x 4 heads checked against the oracle."""
+    padded caches; all 32 heads of 10 sequences (the longest, the shortest
+    and 8 drawn at random) checked against the oracle."""
     c = configs.DECODE
     lens = inputs.lengths(c["batch"], c["len_lo"], c["len_hi"], c["seed"]).to(torch.int32)
     rng = np.random.default_rng(5)
-    bs = [int(lens.argmax()), int(lens.argmin())] + list(rng.choice(c["batch"], 6, replace=False))
-    pairs = [(int(b), int(h)) for b in bs for h in (0, 7, 19, 31)]
+    bs = [int(lens.argmax()), int(lens.argmin())]
+    bs += [int(b) for b in rng.permutation(c["batch"]) if int(b) not in bs][:8]
+    pairs = [(b, h) for b in bs for h in range(c["heads"])]
     _decode_case(c["batch"], c["heads"], c["max_len"], c["d"], lens, c["chunk"], c["seed"], pairs)
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Kernel branches reached only by particular shapes: the longest-first work
+# order (batch * heads a multiple of 8 with a mask, several tiles per head),
+# packed batches whose key lengths differ from their query lengths, a single
+# key for many queries, and windows far wider than any sequence.
+
+
+@pytest.mark.parametrize("causal,W", [(True, -1), (True, 256), (False, 300)])
+def test_backward_headline_shape(causal, W):
+    """B4 H16 N2048 d128: 64 (batch, head) units, so the dK/dV and dQ kernels
+    take their longest-first order under a mask; every element of dQ, dK and
+    dV against the oracle."""
+    c = configs.PREFILL_2K
+    _bwd_case(c["batch"], c["heads"], c["seqlen"], c["seqlen"], c["d"], causal, W, seed=c["seed"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
+    (2, 4, 700, 700, True, -1),
+    (2, 4, 700, 700, True, 150),
+    (1, 8, 600, 600, False, 200),
+    (1, 8, 500, 900, True, -1),    # n_q < n_k
+    (1, 8, 650, 400, True, 100),   # n_q > n_k: rows without keys
+])
+def test_backward_longest_first(d, B, H, n_q, n_k, causal, W):
+    """batch * heads = 8 with several 128-row tiles per head: the masked
+    branch of the backward work order at both head dims."""
+    _bwd_case(B, H, n_q, n_k, d, causal, W, seed=73)
+
+
+@pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
+    (2, 4, 600, 600, True, -1),    # 5 query tiles per head, longest first
+    (1, 8, 700, 700, True, 150),
+    (1, 8, 500, 500, False, 100),  # window only: earlier tiles are the long ones
+    (2, 4, 389, 389, True, -1),    # ragged last tile
+    (1, 8, 450, 800, True, 64),    # n_q < n_k
+    (1, 16, 700, 300, True, -1),   # n_q > n_k: whole tiles without keys
+])
+def test_d64_longest_first(B, H, n_q, n_k, causal, W):
+    """The d = 64 kernel's longest-first order with several tiles per head."""
+    _dense_case(B, H, n_q, n_k, 64, causal, W, torch.bfloat16, seed=81 + n_q + W)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n_new,W", [(400, -1), (600, 200)])
+def test_kvcache_longest_first(d, n_new, W):
+    """KV-cache launches with batch * heads = 8 and several query tiles per
+    head (the longest-first order over caches of different lengths)."""
+    _kvcache_case(2, 4, 1300, d, [1300, 900], n_new, True, W, seed=83)
+
+
+def _varlen_pair_case(lens_q, lens_k, H, d, causal, W, seed):
+    lq, lk = torch.as_tensor(lens_q), torch.as_tensor(lens_k)
+    cu_q, cu_k = inputs.cu_seqlens(lq), inputs.cu_seqlens(lk)
+    q, k, v = inputs.varlen_qkv_pair(lq, lk, H, d, seed)
+    s = configs.default_scale(d)
+    what = f"varlen cross nq{list(lens_q)} nk{list(lens_k)} H{H} d{d} causal{int(causal)} W{W}"
+    announce(what)
+    o, lse = fa.attention_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(),
+                                 max(int(lq.max()), 1), max(int(lk.max()), 1), scale=s,
+                                 causal=causal, window_left=W)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_varlen(_np(q), _np(k), _np(v), cu_q.numpy(), cu_k.numpy(),
+                                             s, causal, W)
+    check(o.cpu(), lse.cpu(), o_ref, lse_ref, torch.bfloat16, what)
+    return o.cpu(), lse.cpu(), cu_q
+
+
+# per sequence: n_k > n_q, n_k < n_q (causal leaves the first rows without
+# keys), n_k = 0, n_q = 0, one key, equal lengths
+VARLEN_Q = [300, 129, 64, 0, 200, 5, 517, 1]
+VARLEN_K = [500, 64, 0, 100, 200, 1, 300, 700]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,W", [(True, -1), (True, 90), (False, -1), (False, 150)])
+def test_varlen_cross_lengths(d, causal, W):
+    """Packed sequences whose key counts differ from their query counts:
+    per-sequence bottom-right alignment delta = n_k - n_q on the varlen path."""
+    o, lse, cu_q = _varlen_pair_case(VARLEN_Q, VARLEN_K, 3, d, causal, W, seed=91)
+    # the sequence with no keys: zeros and -inf
+    a, b = int(cu_q[2]), int(cu_q[3])
+    assert torch.all(o[a:b] == 0) and torch.all(torch.isneginf(lse[:, a:b]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_key_many_queries(d, causal):
+    """seqlen_k = 1: every row that sees the key returns V_0 exactly (p = 1)
+    with lse = scale q . k_0; with the causal mask only the last row sees it."""
+    n_q = 333
+    o, lse, o_ref, lse_ref = _dense_case(2, 2, n_q, 1, d, causal, -1, torch.bfloat16,
+                                         seed=95 + d)
+    _, _, v = inputs.dense_qkv(2, n_q, 1, 2, d, 95 + d, torch.bfloat16)
+    live = slice(n_q - 1, n_q) if causal else slice(0, n_q)
+    assert torch.equal(o[:, live], v.expand(2, n_q, 2, d)[:, live])
+    if causal:
+        assert torch.all(o[:, :n_q - 1] == 0) and torch.all(torch.isneginf(lse[:, :, :n_q - 1]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_near_int_max(d, causal):
+    """window_left = 2^31 - 1 with n_q > n_k: the same result as no window
+    (the kernels' window bound must not wrap around)."""
+    _dense_case(1, 2, 400, 150, d, causal, 2 ** 31 - 1, torch.bfloat16, seed=97)
