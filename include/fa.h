@@ -179,6 +179,38 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
               int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of the per-GPU device array that fa_decode_noalloc keeps its chunk
+ * states in (80 MiB).
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)80 << 20)
+
+/*
+ * fa_decode_noalloc -- fa_decode with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus workspace),
+ * layouts, kernels and results as fa_decode (bit-identical outputs).
+ *   The chunk states live in a static device array of FA_DECODE_SCRATCH_BYTES
+ * per GPU, created when the library's code is loaded on that GPU and held
+ * until the process ends; the call allocates nothing and frees nothing.
+ * Its device address is looked up once per GPU, on the first call whose
+ * stream belongs to that GPU.
+ *   Limit: fa_decode_workspace_size(batch, heads, max_len, d, chunk) must be
+ * at most FA_DECODE_SCRATCH_BYTES, else FA_ERR_WORKSPACE (checked on the host
+ * before any HIP call).  At d = 128 that is about 162k (sequence, head,
+ * chunk) states, e.g. 64 sequences x 32 heads x max_len 32768 with 512-key
+ * chunks (67.6 MB); the same batch in 256-key chunks (135 MB) is rejected.
+ *   Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (other streams,
+ * other threads) race and can return wrong results, so serialise them (one
+ * stream).  Each value a call reads from the array it first writes itself,
+ * so nothing needs clearing between calls.
+ * FA_ERR_LAUNCH also when the array's address cannot be obtained.
+ */
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seqlens_k, void* o, float* lse, int batch, int heads,
+                      int max_len, int d, float scale, int chunk, void* stream);
+
+/*
  * fa_fwd_fp8 -- attention forward (dense) on 8-bit floating-point inputs, the
  * low-precision variant named in "FlashAttention" (aiwiki.page), section
  * "Versions".  q, k, v hold OCP e4m3 codes (1 byte each, the float8_e4m3fn

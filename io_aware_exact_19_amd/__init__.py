@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     FA_ERR_INVALID_ARG,
     FA_ERR_LAUNCH,
     FA_ERR_UNSUPPORTED,
+    FA_DECODE_SCRATCH_BYTES,
     FA_ERR_WORKSPACE,
     FA_OK,
     LIB_PATH,
@@ -21,6 +22,7 @@ from .binding import (  # noqa: F401
     fa_bwd,
     fa_bwd_workspace_size,
     fa_decode,
+    fa_decode_noalloc,
     fa_decode_workspace_size,
     fa_fwd,
     fa_fwd_fp32,

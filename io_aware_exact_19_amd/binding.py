@@ -1,7 +1,8 @@
 """Python binding of libfa.so: argument marshalling only.
 
 The functions named like the C entry points (``fa_fwd``, ``fa_fwd_fp32``,
-``fa_decode``, ``fa_decode_workspace_size``, ``fa_status_string``) take the
+``fa_decode``, ``fa_decode_noalloc``, ``fa_decode_workspace_size``,
+``fa_status_string`` and the others in ``EXPORTED``) take the
 same arguments as in ``include/fa.h``; pointer arguments may be torch tensors
 (their ``data_ptr()``), plain integers or None, and ``stream`` may be a
 ``torch.cuda.Stream``, a raw handle or None (torch's current stream).  They
@@ -30,7 +31,11 @@ FA_ERR_WORKSPACE = -3
 FA_ERR_LAUNCH = -4
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_kvcache", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_decode_workspace_size", "fa_decode", "fa_fwd_fp8", "fa_status_string")
+            "fa_decode_workspace_size", "fa_decode", "fa_decode_noalloc", "fa_fwd_fp8",
+            "fa_status_string")
+
+# bytes of the per-GPU device array behind fa_decode_noalloc
+FA_DECODE_SCRATCH_BYTES = 80 << 20
 
 _lib = None
 
@@ -67,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_decode_workspace_size.restype = Z
     lib.fa_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, Z, P]
     lib.fa_decode.restype = I
+    lib.fa_decode_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.fa_decode_noalloc.restype = I
     lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P]
     lib.fa_fwd_fp8.restype = I
     lib.fa_status_string.argtypes = [I]
@@ -137,6 +144,13 @@ def fa_decode(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d, 
     return load_library().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k),
                                     _ptr(o), _ptr(lse), batch, heads, max_len, d, scale, chunk,
                                     _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d, scale,
+                      chunk, stream=None) -> int:
+    return load_library().fa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(seqlens_k), _ptr(o), _ptr(lse), batch, heads,
+                                            max_len, d, scale, chunk, _stream(stream))
 
 
 def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, batch, heads, seqlen_q, seqlen_k,

@@ -170,9 +170,16 @@ size_t fa_decode_workspace_size(int batch, int heads, int max_len, int d, int ch
   return lse_off + (size_t)batch * heads * max_chunks * sizeof(float);
 }
 
-int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
-              void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
-              int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by fa_decode and fa_decode_noalloc; fills everything of `a`
+// but the workspace pointers.  need = the workspace bytes of the call.
+int decode_common(const void* q, const void* k_cache, const void* v_cache,
+                  const int* seqlens_k, void* o, float* lse, int batch, int heads, int max_len,
+                  int d, float scale, int chunk, fa::DecodeArgs& a, size_t& need,
+                  size_t& lse_off) {
   if (batch < 0 || heads < 0 || max_len < 0 || chunk <= 0) return FA_ERR_INVALID_ARG;
   if (!head_dim_valid(d)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
@@ -186,30 +193,59 @@ int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int
       !aligned(seqlens_k, 4))
     return FA_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_decode_workspace_size(batch, heads, max_len, d, chunk);
-  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
-    return FA_ERR_WORKSPACE;
   const int max_chunks = (max_len + chunk - 1) / chunk;
   if ((long long)batch * heads * max_chunks > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   if ((long long)chunk * heads * d * 2 >= 0x80000000LL) return FA_ERR_UNSUPPORTED;
-
-  fa::DecodeArgs a;
+  need = fa_decode_workspace_size(batch, heads, max_len, d, chunk);
+  lse_off = fa::decode_ws_lse_offset(batch, heads, max_chunks, d);
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
   a.seqlens = seqlens_k;
   a.o = o;
   a.lse = lse;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      fa::decode_ws_lse_offset(batch, heads, max_chunks, d));
+  a.ws_o = nullptr;
+  a.ws_lse = nullptr;
   a.batch = batch;
   a.heads = heads;
   a.max_len = max_len;
   a.max_chunks = max_chunks;
   a.chunk = chunk;
   a.scale_log2 = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_decode(const void* q, const void* k_cache, const void* v_cache, const int* seqlens_k,
+              void* o, float* lse, int batch, int heads, int max_len, int d, float scale,
+              int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  fa::DecodeArgs a;
+  size_t need = 0, lse_off = 0;
+  const int st = decode_common(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d,
+                               scale, chunk, a, need, lse_off);
+  if (st != FA_OK || batch == 0 || heads == 0) return st;
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16))
+    return FA_ERR_WORKSPACE;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
   const hipError_t e = fa::launch_decode(a, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seqlens_k, void* o, float* lse, int batch, int heads,
+                      int max_len, int d, float scale, int chunk, void* stream) {
+  fa::DecodeArgs a;
+  size_t need = 0, lse_off = 0;
+  const int st = decode_common(q, k_cache, v_cache, seqlens_k, o, lse, batch, heads, max_len, d,
+                               scale, chunk, a, need, lse_off);
+  if (st != FA_OK || batch == 0 || heads == 0) return st;
+  if (need > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+  const hipError_t e =
+      fa::launch_decode_scratch(a, d, lse_off, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

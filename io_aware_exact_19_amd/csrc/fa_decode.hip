@@ -26,11 +26,19 @@
 //    their scores are masked to -inf.
 //  * combine kernel: one wave per (sequence, head) merges the chunk states
 //    with the same rescale: weights 2^(lse_c - max), output = weighted mean.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
+
+// Chunk states of the allocation-free entry point: one array per GPU, created
+// with the code object and held until the process ends.  In host code the
+// name `scratch` only stands for the device symbol; its device address comes
+// from hipGetSymbolAddress, once per device (decode_scratch_ptr below).
+static __device__ __attribute__((aligned(256))) char scratch[kDecodeScratchBytes];
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
@@ -266,6 +274,51 @@ hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream) {
   if (d == 128) return launch_d<128>(a, stream);
   if (d == 64) return launch_d<64>(a, stream);
   return hipErrorInvalidValue;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+
+// Device address of `scratch` on `dev`, looked up once per device with that
+// device current (the previous current device is restored).
+hipError_t decode_scratch_ptr(int dev, char** out) {
+  static std::mutex mu;
+  static char* ptrs[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<char*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode_scratch(DecodeArgs a, int d, size_t lse_off, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  char* base = nullptr;
+  if ((e = decode_scratch_ptr(dev, &base)) != hipSuccess) return e;
+  // every chunk state the combine kernel reads is written by the split kernel
+  // of the same call, so the array needs no clearing between calls
+  a.ws_o = reinterpret_cast<float*>(base);
+  a.ws_lse = reinterpret_cast<float*>(base + lse_off);
+  return launch_decode(a, d, stream);
 }
 
 }  // namespace fa

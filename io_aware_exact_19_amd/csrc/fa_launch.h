@@ -53,6 +53,15 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_fwd_fp32(const FwdArgs& a, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int d, hipStream_t stream);
 
+// Size of the static device array that holds the chunk states of the
+// allocation-free decode entry point (one array per GPU, fa_decode.hip).
+constexpr size_t kDecodeScratchBytes = (size_t)80 << 20;
+
+// launch_decode with ws_o / ws_lse placed in that array on the stream's GPU
+// (the caller has checked that the workspace size fits); lse_off is the byte
+// offset of the chunk lse part.
+hipError_t launch_decode_scratch(DecodeArgs a, int d, size_t lse_off, hipStream_t stream);
+
 struct BwdArgs {
   const void* q;       // [batch, seqlen_q, heads, d] bf16
   const void* k;       // [batch, seqlen_k, heads, d] bf16

@@ -250,3 +250,41 @@ def test_fwd_fp8_rejects(lib, bad, code):
 @pytest.mark.parametrize("empty", [dict(batch=0), dict(heads=0), dict(seqlen_q=0)])
 def test_fwd_fp8_empty_is_noop(lib, empty):
     assert _fp8(q=0, k=0, v=0, o=0, descale_q=0, descale_k=0, descale_v=0, **empty) == fa.FA_OK
+
+
+def _dec_na(**kw):
+    args = dict(q=P, k_cache=P, v_cache=P, seqlens_k=P, o=P, lse=P, batch=4, heads=8,
+                max_len=1000, d=128, scale=0.1, chunk=256, stream=NULL_STREAM)
+    args.update(kw)
+    return fa.fa_decode_noalloc(**args)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_DECODE_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlens_k=P + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_INVALID_ARG),
+    (dict(chunk=100), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(max_len=0), fa.FA_ERR_INVALID_ARG),
+    # 64 x 32 heads x 32768 keys in 256-key chunks needs 135 MB of chunk states
+    (dict(batch=64, heads=32, max_len=32768, chunk=256), fa.FA_ERR_WORKSPACE),
+    (dict(batch=0), fa.FA_OK),
+])
+def test_decode_noalloc_rejects(lib, bad, code):
+    assert _dec_na(**bad) == code
+
+
+def test_decode_noalloc_limit_is_the_workspace_size(lib):
+    """The largest accepted call needs at most the array's bytes; one more
+    chunk row of sequences does not fit."""
+    need = fa.fa_decode_workspace_size(64, 32, 32768, 128, 512)
+    assert need <= fa.FA_DECODE_SCRATCH_BYTES
+    assert fa.fa_decode_workspace_size(64, 32, 32768, 128, 256) > fa.FA_DECODE_SCRATCH_BYTES
+    # rejected before any HIP call (only the size differs from an accepted shape)
+    assert _dec_na(batch=64, heads=32, max_len=32768, chunk=256) == fa.FA_ERR_WORKSPACE
