@@ -134,23 +134,49 @@ __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w, i
   }
 }
 
-// Variable-length scheduler: every wave scans the per-sequence tile counts
-// ceil(len_q / rows) from cu_seqlens_q (no host round trip), drops the
-// workgroups past the live total, renumbers the rest XCD-contiguously and
-// finds its (head, sequence, tile).  Head-major order keeps the tiles of one
-// (sequence, head) on one XCD.
+// Inclusive prefix sum across the 64 lanes of a wave on the DPP network: row
+// shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of
+// rows 0 and 2 added to rows 1 and 3 and the last lane of row 1 to rows 2
+// and 3 (row broadcasts).  Six adds, no LDS round trips.
+__device__ __forceinline__ int wave_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Variable-length scheduler: every wave reads the per-sequence offsets from
+// cu_seqlens_q/k (64 sequences per round, all four bounds of a sequence in
+// flight together; no host round trip), counts each sequence's query tiles
+// ceil(len_q / rows), drops the workgroups past the live total, renumbers the
+// rest XCD-contiguously and finds its (head, sequence, tile).  Head-major
+// order keeps the tiles of one (sequence, head) on one XCD.  With at most 64
+// sequences the offsets are read once and the lookup works on registers.
 __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
   const int nseq = a.batch;
-  int total = 0;
-  for (int s0 = 0; s0 < nseq; s0 += 64) {
+  int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = 0, nt = 0, inc = 0;
+  auto load_chunk = [&](int s0) {
     const int s = s0 + lane;
-    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), rows) : 0;
-    const int inc = wave_inclusive_scan(nt, lane);
-    total += __shfl(inc, 63, 64);
+    const bool ok = s < nseq;
+    cq0 = ok ? a.cu_q[s] : 0;
+    cq1 = ok ? a.cu_q[s + 1] : 0;
+    ck0 = ok ? a.cu_k[s] : 0;
+    ck1 = ok ? a.cu_k[s + 1] : 0;
+    nt = ok ? ceil_div(max(cq1 - cq0, 0), rows) : 0;
+    inc = wave_scan_dpp(nt);
+  };
+  int total = 0, total_q = 0;
+  for (int s0 = 0; s0 < nseq; s0 += 64) {
+    load_chunk(s0);
+    total += __builtin_amdgcn_readlane(inc, 63);
+    if (s0 + 64 >= nseq) total_q = __builtin_amdgcn_readlane(cq1, nseq - 1 - s0);
   }
-  // every lane holds the same values; say so, so that the work decode stays
-  // in scalar registers (else the tile loop and the buffer descriptors built
-  // from it would be treated as divergent)
+  // uniform by construction; say so, so that the work decode stays in scalar
+  // registers (else the tile loop and the buffer descriptors built from it
+  // would be treated as divergent)
   total = __builtin_amdgcn_readfirstlane(total);
   const long long live = (long long)total * a.heads;
   if ((long long)blockIdx.x >= live) return false;
@@ -159,27 +185,24 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
   const int g = id - w.h * total;
   int base = 0;
   for (int s0 = 0; s0 < nseq; s0 += 64) {
-    const int s = s0 + lane;
-    const int nt = s < nseq ? ceil_div(max(a.cu_q[s + 1] - a.cu_q[s], 0), rows) : 0;
-    const int inc = wave_inclusive_scan(nt, lane) + base;
-    const int exc = inc - nt;
-    const unsigned long long hit = __ballot(s < nseq && g >= exc && g < inc);
+    if (nseq > 64) load_chunk(s0);  // else chunk 0 is still in registers
+    const int end = base + inc, beg = end - nt;
+    const unsigned long long hit = __ballot(s0 + lane < nseq && g >= beg && g < end);
     if (hit) {
       const int src = __builtin_ctzll(hit);
-      const int seq = s0 + src;
-      const int t = g - __builtin_amdgcn_readfirstlane(__shfl(exc, src, 64));
-      const int ntq = __builtin_amdgcn_readfirstlane(__shfl(nt, src, 64));
-      const int cq0 = a.cu_q[seq], cq1 = a.cu_q[seq + 1];
-      const int ck0 = a.cu_k[seq], ck1 = a.cu_k[seq + 1];
+      const int t = g - __builtin_amdgcn_readlane(beg, src);
+      const int ntq = __builtin_amdgcn_readlane(nt, src);
+      const int q0 = __builtin_amdgcn_readlane(cq0, src), q1 = __builtin_amdgcn_readlane(cq1, src);
+      const int k0 = __builtin_amdgcn_readlane(ck0, src), k1 = __builtin_amdgcn_readlane(ck1, src);
       w.qt = ntq - 1 - t;
-      w.n_q = cq1 - cq0;
-      w.n_k = max(ck1 - ck0, 0);
-      w.q_row0 = cq0;
-      w.k_row0 = ck0;
-      w.lse_base = (long long)w.h * a.cu_q[nseq] + cq0;
+      w.n_q = q1 - q0;
+      w.n_k = max(k1 - k0, 0);
+      w.q_row0 = q0;
+      w.k_row0 = k0;
+      w.lse_base = (long long)w.h * total_q + q0;
       return true;
     }
-    base = __builtin_amdgcn_readfirstlane(__shfl(inc, 63, 64));
+    base += __builtin_amdgcn_readlane(inc, 63);
   }
   return false;
 }
@@ -301,6 +324,24 @@ __device__ __forceinline__ float tree_max(const f32x16_t (&v)[N]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a[i] = fmaxf(a[i], fmaxf(fmaxf(v[n][4 * i], v[n][4 * i + 1]), fmaxf(v[n][4 * i + 2], v[n][4 * i + 3])));
+  return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+}
+
+// Maximum of N x 16 values with three-input maxima (v_max3_f32, two new
+// values per instruction) in four independent chains.
+template <int N>
+__device__ __forceinline__ float tree_max3(const f32x16_t (&v)[N]) {
+  float a[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a[c] = fmaxf(v[0][4 * c], v[0][4 * c + 1]);
+#pragma unroll
+  for (int n = 0; n < N; ++n)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i0 = n == 0 ? 4 * c + 2 : 4 * c;
+      a[c] = __builtin_fmaxf(__builtin_fmaxf(a[c], v[n][i0]), v[n][i0 + 1]);
+      if (n > 0) a[c] = __builtin_fmaxf(__builtin_fmaxf(a[c], v[n][4 * c + 2]), v[n][4 * c + 3]);
+    }
   return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
 }
 
@@ -957,6 +998,8 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
         v_off[db][ks][u] = vtile_off<D>(r, d >> 3) + (d & 7) * 2;
       }
 
+  const int kt_first = max(t_lo, w_lo / kBC);  // the wave's first live tile
+
   // one K/V tile: S^T = K Q^T, mask, online softmax update, O^T += V^T P^T
   auto compute_tile = [&](int kt, const char* kb_lds, const char* vb_lds) {
     const int k0 = kt * kBC;
@@ -975,28 +1018,39 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
       }
     }
 
-    // element mask, only on tiles crossing a mask boundary
-    const bool need_mask = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta) ||
-                           (W >= 0 && k0 < wq_last + delta - W);
-    if (need_mask) {
-      // allowed keys of this lane's row: [lo, hi]; key kj = k0 + 8 half + c
-      // is allowed iff 0 <= kj - lo <= hi - lo, one unsigned compare per key
-      // (kj < lo wraps to a large value); a row with hi < lo allows none.
-      // Three vector instructions per key against five for two sign tests;
-      // this kernel has the scalar registers the compare results take.
+    // element mask, only on tiles crossing a mask boundary.  Key kj = k0 +
+    // 8 half + c of this lane's row is allowed iff lo <= kj <= hi, i.e.
+    // a_lo <= c <= a_hi with per-lane a_lo = lo - k0 - 8 half and a_hi =
+    // hi - k0 - 8 half: one compare of the register's constant offset c with
+    // a per-lane value and one select per key, per bound the tile crosses
+    const bool cut_hi = (k0 + kBC > n_k) || (causal && k0 + kBC - 1 > wq0 + delta);
+    const bool cut_lo = W >= 0 && k0 < wq_last + delta - W;
+    if (cut_hi || cut_lo) {
       int hi = n_k - 1, lo = 0;
       if (causal) hi = min(hi, qi + delta);
       if (W >= 0) lo = max(lo, qi + delta - W);
-      const int span = hi - lo;
-      const uint32_t e = span < 0 ? 0x80000000u : (uint32_t)(k0 + 8 * half - lo);
-      const uint32_t range = span < 0 ? 0u : (uint32_t)span;
+      const int a_hi = hi - k0 - 8 * half, a_lo = lo - k0 - 8 * half;
+      if (!cut_lo) {
 #pragma unroll
-      for (int kb = 0; kb < kBC / 32; ++kb)
+        for (int kb = 0; kb < kBC / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t c = kb * 32 + 16 * (r >> 3) + (r & 7);
-          if (e + c > range) sacc[kb][r] = kNegInf;
-        }
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 16 * (r >> 3) + (r & 7) > a_hi) sacc[kb][r] = kNegInf;
+      } else if (!cut_hi) {
+#pragma unroll
+        for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 16 * (r >> 3) + (r & 7) < a_lo) sacc[kb][r] = kNegInf;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < kBC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = kb * 32 + 16 * (r >> 3) + (r & 7);
+            if (c > a_hi || c < a_lo) sacc[kb][r] = kNegInf;
+          }
+      }
     }
 
     // online softmax update, base 2, lazy reference max: probabilities
@@ -1005,6 +1059,10 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
     // row's first live tile, whose reference is -inf, or a jump of the row
     // max) the reference moves to the tile max, the state is rescaled and
     // the probabilities recomputed
+    // the wave's first live tile takes its row max as the reference at once
+    // (against -inf every probability would overflow and be recomputed); a
+    // row with no allowed key there keeps -inf and goes the slow way below
+    if (kt == kt_first) m_run = max_halves(tree_max3<kBC / 32>(sacc)) * c2;
     float p[kBC / 32][16];
 #pragma unroll
     for (int kb = 0; kb < kBC / 32; ++kb)
