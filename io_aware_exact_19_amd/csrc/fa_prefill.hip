@@ -153,11 +153,26 @@ __device__ __forceinline__ int wave_scan_dpp(int x) {
 // flight together; no host round trip), counts each sequence's query tiles
 // ceil(len_q / rows), drops the workgroups past the live total, renumbers the
 // rest XCD-contiguously and finds its (head, sequence, tile).  Head-major
-// order keeps the tiles of one (sequence, head) on one XCD.  With at most 64
-// sequences the offsets are read once and the lookup works on registers.
+// order keeps the tiles of one (sequence, head) on one XCD; the hardware
+// starts a new workgroup whenever one ends, so the order is also the order
+// in which work is handed out.  With at most 64 sequences the offsets are read
+// once and the lookup works on registers.
+//
+// Order within a head: with a causal mask and a left window of W keys, a
+// query tile t (rows beginning at t * rows) needs keys from t * rows + delta
+// - W on, so every tile from kSat = ceil((W + 1) / rows) on costs the same
+// (about W + rows keys) while the first kSat tiles of a sequence ramp up
+// from one key tile.  The head's items run as: the full-cost tiles of every
+// sequence (sequence order, latest tile first, so neighbouring items share
+// key tiles), then the short ramp tiles from the longest down (tile kSat - 1
+// of every sequence, then kSat - 2, ...), so the last items handed out are
+// the shortest and workgroups finish close together.  Without such a window
+// the order is sequence by sequence, latest tile first.
 __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
   const int nseq = a.batch;
-  int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = 0, nt = 0, inc = 0;
+  // ramp length in tiles (0: no reordering)
+  const int ksat = a.causal && a.window_left >= 0 ? ceil_div(a.window_left + 1, rows) : 0;
+  int cq0 = 0, cq1 = 0, ck0 = 0, ck1 = 0, nt = 0, nl = 0, inc = 0;
   auto load_chunk = [&](int s0) {
     const int s = s0 + lane;
     const bool ok = s < nseq;
@@ -166,45 +181,75 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
     ck0 = ok ? a.cu_k[s] : 0;
     ck1 = ok ? a.cu_k[s + 1] : 0;
     nt = ok ? ceil_div(max(cq1 - cq0, 0), rows) : 0;
-    inc = wave_scan_dpp(nt);
+    nl = ksat > 0 ? max(nt - ksat, 0) : nt;  // full-cost tiles, handed out first
+    inc = wave_scan_dpp(nl);
   };
-  int total = 0, total_q = 0;
+  int total = 0, total_long = 0, total_q = 0, max_nt = 0;
   for (int s0 = 0; s0 < nseq; s0 += 64) {
     load_chunk(s0);
-    total += __builtin_amdgcn_readlane(inc, 63);
+    total_long += __builtin_amdgcn_readlane(inc, 63);
+    total += __builtin_amdgcn_readlane(wave_scan_dpp(nt), 63);
+    int mx = nt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+    max_nt = max(max_nt, mx);
     if (s0 + 64 >= nseq) total_q = __builtin_amdgcn_readlane(cq1, nseq - 1 - s0);
   }
   // uniform by construction; say so, so that the work decode stays in scalar
   // registers (else the tile loop and the buffer descriptors built from it
   // would be treated as divergent)
   total = __builtin_amdgcn_readfirstlane(total);
+  total_long = __builtin_amdgcn_readfirstlane(total_long);
+  max_nt = __builtin_amdgcn_readfirstlane(max_nt);
   const long long live = (long long)total * a.heads;
   if ((long long)blockIdx.x >= live) return false;
   const int id = xcd_contiguous(blockIdx.x, (int)live);
   w.h = id / total;
   const int g = id - w.h * total;
-  int base = 0;
-  for (int s0 = 0; s0 < nseq; s0 += 64) {
-    if (nseq > 64) load_chunk(s0);  // else chunk 0 is still in registers
-    const int end = base + inc, beg = end - nt;
-    const unsigned long long hit = __ballot(s0 + lane < nseq && g >= beg && g < end);
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      const int t = g - __builtin_amdgcn_readlane(beg, src);
-      const int ntq = __builtin_amdgcn_readlane(nt, src);
-      const int q0 = __builtin_amdgcn_readlane(cq0, src), q1 = __builtin_amdgcn_readlane(cq1, src);
-      const int k0 = __builtin_amdgcn_readlane(ck0, src), k1 = __builtin_amdgcn_readlane(ck1, src);
-      w.qt = ntq - 1 - t;
-      w.n_q = q1 - q0;
-      w.n_k = max(k1 - k0, 0);
-      w.q_row0 = q0;
-      w.k_row0 = k0;
-      w.lse_base = (long long)w.h * total_q + q0;
-      return true;
+  int src = -1, qt = 0;
+  if (g < total_long) {
+    // full-cost tile number t of its sequence, latest first
+    int base = 0;
+    for (int s0 = 0; s0 < nseq; s0 += 64) {
+      if (nseq > 64) load_chunk(s0);  // else chunk 0 is still in registers
+      const int end = base + inc, beg = end - nl;
+      const unsigned long long hit = __ballot(s0 + lane < nseq && g >= beg && g < end);
+      if (hit) {
+        src = __builtin_ctzll(hit);
+        qt = __builtin_amdgcn_readlane(nt, src) - 1 - (g - __builtin_amdgcn_readlane(beg, src));
+        break;
+      }
+      base += __builtin_amdgcn_readlane(inc, 63);
     }
-    base += __builtin_amdgcn_readlane(inc, 63);
+  } else {
+    // ramp tiles: level lvl = ksat - 1, ksat - 2, ..., 0 holds tile lvl of
+    // every sequence with more than lvl tiles, in sequence order
+    int r = g - total_long;
+    for (int lvl = min(ksat, max_nt) - 1; lvl >= 0 && src < 0; --lvl) {
+      for (int s0 = 0; s0 < nseq; s0 += 64) {
+        if (nseq > 64) load_chunk(s0);  // else chunk 0 is still in registers
+        unsigned long long has = __ballot(s0 + lane < nseq && nt > lvl);
+        const int cnt = __builtin_popcountll(has);
+        if (r < cnt) {
+          for (int k = r; k > 0; --k) has &= has - 1;  // drop the r lowest owners
+          src = __builtin_ctzll(has);
+          qt = lvl;
+          break;
+        }
+        r -= cnt;
+      }
+    }
   }
-  return false;
+  if (src < 0) return false;
+  const int q0 = __builtin_amdgcn_readlane(cq0, src), q1 = __builtin_amdgcn_readlane(cq1, src);
+  const int k0 = __builtin_amdgcn_readlane(ck0, src), k1 = __builtin_amdgcn_readlane(ck1, src);
+  w.qt = qt;
+  w.n_q = q1 - q0;
+  w.n_k = max(k1 - k0, 0);
+  w.q_row0 = q0;
+  w.k_row0 = k0;
+  w.lse_base = (long long)w.h * total_q + q0;
+  return true;
 }
 
 // One K or V tile in LDS: kBC rows x D bf16, row-major as in HBM, with the
