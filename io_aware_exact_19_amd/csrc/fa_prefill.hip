@@ -324,6 +324,17 @@ __device__ __forceinline__ void dma16(const u32x4_t& rsrc_in, uint32_t voff, uin
       : "memory");
 }
 
+// A pointer every lane holds the same value of, moved to scalar registers, so
+// that buffer descriptors built from it are known to be uniform (otherwise
+// the compiler wraps each buffer access in a loop over the distinct values).
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)p);
 }
@@ -932,11 +943,12 @@ __device__ __forceinline__ void issue_tile4(const uint16_t* kg, const uint16_t* 
                                            int lane) {
   using T = BfTile<D, kQThreads>;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const uint32_t nrec = (uint32_t)min(n_k - k0, kBC) * row_bytes;
+  const uint32_t nrec =
+      __builtin_amdgcn_readfirstlane((uint32_t)min(n_k - k0, kBC) * row_bytes);
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
+      (void*)uniform_ptr(kg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
+      (void*)uniform_ptr(vg + (long long)k0 * rs), 0, nrec, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < T::kLoads; ++i) {
     const int blk = i * 4 + wave;  // 1 KB block of the tile written by this wave
@@ -1004,9 +1016,10 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
   bf16x8_t qf[D / 16];
   {
     const uint32_t row_bytes = (uint32_t)(rs * 2);
-    const uint32_t nrec = (uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes;
+    const uint32_t nrec =
+        __builtin_amdgcn_readfirstlane((uint32_t)max(min(n_q - wq0, 32), 0) * row_bytes);
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
+        (void*)uniform_ptr(qg + (long long)wq0 * rs), 0, nrec, kRsrcWord3);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(
