@@ -239,6 +239,8 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
     return f;
   };
 
+  const int kt_first = max(t_lo, w_lo / kBC8);  // the wave's first live tile
+
   auto compute_tile = [&](int kt, const char* kl, const char* vl) {
     const int k0 = kt * kBC8;
     if (!(wave_live && k0 < w_hi && k0 + kBC8 > w_lo)) return;  // nothing allowed for this wave
@@ -251,24 +253,51 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(Fp8Args a) {
       asm volatile("" : "+v"(s[kb]) : "v"(a0));
       s[kb] = mma8(frag(kl, k_off[kb][1][0], k_off[kb][1][1]), qf[1], s[kb]);
     }
-    // this lane's keys: k0 + 32 half + j, j = 16 kb + r
-    const bool need_mask = (k0 + kBC8 > n_k) || (causal && k0 + kBC8 - 1 > wq0 + delta) ||
-                           (W >= 0 && k0 < wq_last + delta - W);
-    if (need_mask) {
+    // this lane's keys: kj = k0 + 32 half + c, c = 16 kb + r, allowed iff
+    // lo <= kj <= hi, i.e. a_lo <= c <= a_hi with per-lane a_lo = lo - k0 -
+    // 32 half, a_hi = hi - k0 - 32 half: one compare of the register's
+    // constant offset c with a per-lane value and one select per key, per
+    // bound the tile crosses
+    const bool cut_hi = (k0 + kBC8 > n_k) || (causal && k0 + kBC8 - 1 > wq0 + delta);
+    const bool cut_lo = W >= 0 && k0 < wq_last + delta - W;
+    if (cut_hi || cut_lo) {
       int hi = n_k - 1, lo = 0;
       if (causal) hi = min(hi, qi + delta);
       if (W >= 0) lo = max(lo, qi + delta - W);
-      // key kj = k0 + 32 half + j is allowed iff 0 <= kj - lo <= hi - lo: one
-      // unsigned compare per key (kj < lo wraps to a large value); a row
-      // with hi < lo allows none
-      const int span = hi - lo;
-      const uint32_t e = span < 0 ? 0x80000000u : (uint32_t)(k0 + 32 * half - lo);
-      const uint32_t range = span < 0 ? 0u : (uint32_t)span;
+      const int a_hi = hi - k0 - 32 * half, a_lo = lo - k0 - 32 * half;
+      if (!cut_lo) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (e + (uint32_t)(16 * kb + r) > range) s[kb][r] = kNegInf;
+          for (int r = 0; r < 16; ++r)
+            if (16 * kb + r > a_hi) s[kb][r] = kNegInf;
+      } else if (!cut_hi) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (16 * kb + r < a_lo) s[kb][r] = kNegInf;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 16 * kb + r;
+            if (c > a_hi || c < a_lo) s[kb][r] = kNegInf;
+          }
+      }
+    }
+    // the wave's first live tile takes its row max as the reference at once
+    // (against -inf every probability would overflow and be recomputed); a
+    // row with no allowed key there keeps -inf and goes the slow way below
+    if (kt == kt_first) {
+      float a4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        a4[c] = fmaxf(fmaxf(fmaxf(s[0][4 * c], s[0][4 * c + 1]), fmaxf(s[0][4 * c + 2], s[0][4 * c + 3])),
+                      fmaxf(fmaxf(s[1][4 * c], s[1][4 * c + 1]), fmaxf(s[1][4 * c + 2], s[1][4 * c + 3])));
+      const float mt = fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3]));
+      m_run = fmaxf(mt, swap_halves(mt)) * c2;
     }
     float p[2][16];
 #pragma unroll
