@@ -27,7 +27,11 @@ Every workload first runs back to back for ``--settle-ms`` (default 400 ms)
 so that the engine clock has left its idle ramp before the warmup steps.
 
 ``--profile-target NAME`` runs only NAME's launches (plus, with
-``--calibrate-copy``, a plain device copy of known size) for rocprofv3.
+``--calibrate-copy``, a plain device copy of known size) for rocprofv3;
+``--trace-summary`` turns its kernel trace into the committed summary.
+``--profile-target prefill_sweep`` runs the headline shape at N = 1024 ...
+8192 and ``--sweep-summary`` fits the launch time per key step, per query
+tile and per launch from its kernel trace.
 ``--pmc-summary FETCH_DIR WRITE_DIR`` turns two ``rocprofv3 --pmc`` runs into
 the committed traffic summary under profiles/; ``--mfma-summary UTIL_DIR
 RAW_DIR`` does the same for the matrix-pipe utilisation counters, which the
@@ -476,6 +480,139 @@ def time_evicted(torch, w, launches=40, warmup=10, evict_bytes=1 << 30):
     return statistics.median(a.elapsed_time(b) for a, b in pairs[warmup:])
 
 
+# B4 H16 d128 bf16 non-causal prefill at these lengths: 1, 2, 4 and 8 query
+# tiles of 256 rows per workgroup of the persistent grid (256 workgroups),
+# each tile N / 64 key steps long
+SWEEP_N = (1024, 2048, 4096, 8192)
+SWEEP_ROWS_PER_ITEM = 256
+SWEEP_WGS = 256
+SWEEP_KEYS_PER_STEP = 64
+# matrix cycles of one key step on one SIMD: two waves (one per lock-step
+# group) x 32 products of 32x32x16 at 32 cycles each
+SWEEP_MFMA_CYCLES_PER_STEP = 2 * 32 * 32
+
+
+def profile_sweep(torch, fa, inputs, configs, args):
+    """The headline shape at the lengths of SWEEP_N, one after another, each
+    settled, warmed up and timed like a bench workload; before the N = 2048
+    shape's timing, the engine clock while that shape runs back to back.
+    Logs each shape's launch count and the position of its timed launches,
+    so that a kernel trace of the run can be split by shape."""
+    for n in SWEEP_N:
+        cfg = dict(configs.PREFILL_2K, seqlen=n, name=f"dense_bf16_b4_h16_n{n}_d128")
+        w = make_dense(torch, fa, inputs, configs, cfg, False)
+        count = [0]
+        base = w.launch
+
+        def counted(base=base, count=count):
+            count[0] += 1
+            base()
+
+        w.launch = counted
+        if n == 2048:
+            mhz, watts, snaps, err = measure_clock(torch, w, args.clock_s)
+            log(f"[sweep] clock n={n} mhz={mhz} socket_w={watts} snapshots={snaps} "
+                f"error={err}")
+        if args.settle_ms > 0:
+            settle(torch, w, args.settle_ms)
+        for _ in range(args.warmup):
+            w.launch()
+        first = count[0]
+        _, mean_ms, _ = time_launches(torch, w, args.steps, 0, 0.0)
+        log(f"[sweep] n={n} launches={count[0]} timed_first={first} timed={args.steps} "
+            f"event_mean_ms={mean_ms:.5f} tflops={rate(w, mean_ms):.2f}")
+        del w
+        torch.cuda.empty_cache()
+    return 0
+
+
+def sweep_summary(kt_dir, log_path, out_path, cmd):
+    """Split the kernel trace of a ``--profile-target prefill_sweep`` run by
+    shape, take each shape's mean duration over its timed launches, and fit
+    launch time = steps * t + items * x + c (per workgroup: steps of 64 keys,
+    query tiles).  With the engine clock of the same run this splits the
+    headline's fraction of the published peak into three factors: clock /
+    2.4 GHz, the share of the launch spent in the key loop, and the matrix
+    pipe's share of a loop step's cycles."""
+    import numpy as np
+
+    rows = []
+    for path in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(r for r in csv.DictReader(f)
+                        if "fwd_bf16_kernel<128, false>" in r["Kernel_Name"])
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    blocks, clock = [], None
+    with open(log_path) as f:
+        for line in f:
+            if not line.startswith("[sweep]"):
+                continue
+            kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+            if line.startswith("[sweep] clock"):
+                clock = kv
+            else:
+                blocks.append({k: float(v) for k, v in kv.items()})
+    total = sum(int(b["launches"]) for b in blocks)
+    if total != len(rows):
+        raise SystemExit(f"trace holds {len(rows)} prefill dispatches, the log names {total}")
+    pos, pts = 0, []
+    for b in blocks:
+        n = int(b["n"])
+        lo = pos + int(b["timed_first"])
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+             for r in rows[lo:lo + int(b["timed"])]]
+        pos += int(b["launches"])
+        items = 4 * 16 * n // SWEEP_ROWS_PER_ITEM // SWEEP_WGS
+        steps = items * n // SWEEP_KEYS_PER_STEP
+        pts.append((n, steps, items, statistics.mean(d), statistics.median(d),
+                    b["event_mean_ms"] * 1e3))
+    a = np.array([[p[1], p[2], 1.0] for p in pts])
+    y = np.array([p[3] for p in pts])
+    (t, x, c), *_ = np.linalg.lstsq(a, y, rcond=None)
+    fit = a @ np.array([t, x, c])
+    lines = ["# rocprofv3 kernel trace: bf16 prefill B4 H16 d128 non-causal at N = "
+             + " / ".join(str(n) for n in SWEEP_N) + ", persistent grid of 256 workgroups",
+             f"command: {cmd}",
+             "(per shape: the timed launches only, located by the launch counts the run logged)",
+             "",
+             f"{'N':>6s} {'steps/WG':>9s} {'items/WG':>9s} {'trace_mean_us':>14s} "
+             f"{'trace_median_us':>16s} {'event_mean_us':>14s} {'fit_us':>8s}"]
+    for p, fv in zip(pts, fit):
+        lines.append(f"{p[0]:6d} {p[1]:9d} {p[2]:9d} {p[3]:14.2f} {p[4]:16.2f} {p[5]:14.2f} "
+                     f"{fv:8.2f}")
+    lines += ["",
+              "least-squares fit of launch time = steps * t + items * x + c:",
+              f"  t_us_per_step: {t:.4f}",
+              f"  x_us_per_item: {x:.3f}",
+              f"  c_us_per_launch: {c:.3f}"]
+    mhz = float(clock["mhz"]) if clock and clock.get("mhz") not in (None, "None") else None
+    n2 = next(p for p in pts if p[0] == 2048)
+    loop_share = n2[1] * t / n2[3]
+    lines += [f"engine_clock_mhz (amdsmi, N = 2048 back to back): {clock.get('mhz') if clock else None}"
+              f" socket_w: {clock.get('socket_w') if clock else None}"
+              f" tables: {clock.get('snapshots') if clock else None}"]
+    frac = (4 * 128 * 4 * 16 * 2048 * 2048) / (n2[3] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+    lines += ["decomposition of the N = 2048 launch:",
+              f"  frac_of_2500_tflops: {frac:.4f}",
+              f"  loop_share (steps * t / launch): {loop_share:.4f}"]
+    if mhz:
+        cyc = t * mhz
+        # 256 CUs x 4 SIMDs x 1024 FLOP per cycle at 2.4 GHz is 2516.6
+        # TFLOP/s, published rounded down to 2500
+        rounding = 256 * 4 * 1024 * PEAK_CLOCK_MHZ * 1e6 / 1e12 / PEAK_BF16_TFLOPS
+        occ = SWEEP_MFMA_CYCLES_PER_STEP / cyc
+        lines += [f"  clock_factor (clock / 2400 MHz): {mhz / PEAK_CLOCK_MHZ:.4f}",
+                  f"  cycles_per_step: {cyc:.0f}",
+                  f"  loop_mfma_occupancy ({SWEEP_MFMA_CYCLES_PER_STEP} / cycles_per_step): "
+                  f"{occ:.4f}",
+                  f"  peak_rounding (2516.6 / 2500): {rounding:.4f}",
+                  f"  product: {mhz / PEAK_CLOCK_MHZ * loop_share * occ * rounding:.4f}"]
+    lines.append(f"kernel_source_sha256: {sha256(PREFILL_KERNEL_SRC)}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def rate(w, ms):
     scale = 1e12 if w.unit == "TFLOP/s" else 1e9
     return w.work / (ms * 1e-3) / scale
@@ -680,11 +817,31 @@ def _kernel_short(name):
     return name.replace("fa::(anonymous namespace)::", "").split("(")[0]
 
 
+def _agent_info(d):
+    """(shader arrays, SIMDs) of the GPU agent from a rocprofv3 output dir."""
+    for path in glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if str(r.get("Name", "")).startswith("gfx"):
+                    return int(r.get("Array_Count") or 0), int(r.get("Simd_Count") or 0)
+    return 0, 0
+
+
 def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
     """Matrix-pipe utilisation of every library kernel of one workload from two
     rocprofv3 --pmc passes: the derived MfmaUtil (MFMA busy cycles over all
     SIMDs / (GPU active cycles x SIMDs)), and raw counters, medians per
-    dispatch (GRBM_GUI_ACTIVE comes back summed over the XCDs)."""
+    dispatch (GRBM_GUI_ACTIVE comes back summed over the XCDs).
+
+    Clock: the SQ counters come back summed over the shader arrays, and
+    SQ_BUSY_CYCLES / arrays / dispatch time is the shader clock the kernel
+    ran at (it agrees with the GPU metrics table's engine clock, ~1.8 GHz
+    under the prefill kernels); GRBM_GUI_ACTIVE / XCDs / dispatch time reads
+    ~2.05 GHz, so GRBM_GUI_ACTIVE does not tick at the shader clock, and the
+    derived MfmaUtil, which divides by it, understates the matrix pipes'
+    busy share.  The summary therefore also reports that share against
+    shader cycles: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x SQ_BUSY_CYCLES /
+    arrays)."""
     util = {}
     for r in _pmc_rows(util_dir):
         if r.get("Counter_Name") == "MfmaUtil" and "fa::" in r.get("Kernel_Name", ""):
@@ -717,7 +874,18 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
         if "SQ_INSTS_VALU_MFMA_MOPS_F8" in med:
             lines.append(f"  mfma_flops_f8: {med['SQ_INSTS_VALU_MFMA_MOPS_F8'] * 512:.0f}")
         if k in dur:
-            lines.append(f"  dispatch_us_under_counters: {statistics.median(dur[k]) * 1e6:.2f}")
+            us = statistics.median(dur[k]) * 1e6
+            lines.append(f"  dispatch_us_under_counters: {us:.2f}")
+            arrays, simds = _agent_info(raw_dir)
+            if arrays and simds and "SQ_BUSY_CYCLES" in med and us > 0:
+                shader_cycles = med["SQ_BUSY_CYCLES"] / arrays
+                lines.append(f"  shader_arrays: {arrays}  simds: {simds}")
+                lines.append(f"  shader_clock_mhz_from_sq_busy: {shader_cycles / us:.1f}")
+                if "GRBM_GUI_ACTIVE" in med:
+                    lines.append(f"  grbm_gui_active_mhz_per_xcd: {med['GRBM_GUI_ACTIVE'] / 8 / us:.1f}")
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+                    busy = 100.0 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * shader_cycles)
+                    lines.append(f"  mfma_busy_pct_of_shader_cycles: {busy:.2f}")
     src = (FP8_KERNEL_SRC if target.startswith("fp8") else
            BACKWARD_KERNEL_SRC if target.startswith("backward") else PREFILL_KERNEL_SRC)
     lines.append(f"kernel_source: {os.path.relpath(src, ROOT)}")
@@ -725,6 +893,54 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def trace_summary(kt_dir, log_path, target, out_path, cmd, title):
+    """The library kernels' rows of a rocprofv3 --kernel-trace --stats run of
+    ``--profile-target`` (calls, average / min / max / stddev duration in
+    microseconds), with the bench's own event timing from the same run."""
+    rows = []
+    for path in glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(r for r in csv.DictReader(f) if "fa::" in r.get("Name", ""))
+    prof = []
+    if os.path.exists(log_path):
+        with open(log_path) as f:
+            prof = [ln.strip() for ln in f if ln.startswith("[profile]")]
+    lines = [f"# rocprofv3 kernel trace: {title}",
+             f"command: {cmd}",
+             "(calls include the settle launches that precede the timed ones)",
+             "",
+             f"{'kernel':64s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+             f"{'stddev_us':>10s}"]
+    for r in rows:
+        lines.append(f"{_kernel_short(r['Name']):64s} {r['Calls']:>7s} "
+                     f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['StdDev']) / 1e3:10.2f}")
+    lines += ["", "bench.py's own event timing in the same run:", *prof]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_summary_value(summary, src, kernel, key):
+    """A per-kernel value of a committed counter summary, or None when absent
+    or taken on another version of the kernel source."""
+    if not os.path.exists(summary):
+        return None
+    vals, cur, sha = {}, None, None
+    with open(summary) as f:
+        for line in f:
+            k, _, val = line.strip().partition(":")
+            if k == "kernel":
+                cur = val.strip()
+            elif k == key and cur:
+                vals[cur] = float(val)
+            elif k == "kernel_source_sha256":
+                sha = val.strip()
+    if sha != sha256(src):
+        return None
+    return vals.get(kernel)
 
 
 def read_mfma_util(summary, src, kernel):
@@ -764,7 +980,7 @@ def main():
     ap.add_argument("--profile-target", default=None,
                     choices=["prefill_2k", "prefill_2k_causal", "long_8k", "varlen", "small_fp32",
                              "decode", "kvcache", "backward", "backward_causal", "fp8",
-                             "fp8_causal"])
+                             "fp8_causal", "prefill_sweep"])
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-target", default="prefill_2k")
@@ -772,7 +988,21 @@ def main():
     ap.add_argument("--pmc-cmd", default="")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("UTIL_DIR", "RAW_DIR"))
     ap.add_argument("--algo-flops", type=int, default=0)
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KT_DIR", "LOG"),
+                    help="write the kernel-trace summary of a --profile-target run")
+    ap.add_argument("--trace-title", default="")
+    ap.add_argument("--sweep-summary", nargs=2, metavar=("KT_DIR", "LOG"),
+                    help="write the length-sweep summary of a --profile-target prefill_sweep run")
     args = ap.parse_args()
+
+    if args.sweep_summary:
+        sweep_summary(args.sweep_summary[0], args.sweep_summary[1], args.pmc_out, args.pmc_cmd)
+        return 0
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], args.trace_summary[1], args.pmc_target,
+                      args.pmc_out, args.pmc_cmd, args.trace_title)
+        return 0
 
     if args.mfma_summary:
         mfma_summary(args.mfma_summary[0], args.mfma_summary[1], args.pmc_target, args.pmc_out,
@@ -820,6 +1050,9 @@ def main():
         "fp8": lambda: make_fp8(torch, fa, inputs, configs, configs.PREFILL_2K),
         "fp8_causal": lambda: make_fp8(torch, fa, inputs, configs, configs.PREFILL_2K, causal=True),
     }
+
+    if args.profile_target == "prefill_sweep":
+        return profile_sweep(torch, fa, inputs, configs, args)
 
     if args.profile_target:
         w = builders[args.profile_target]()
@@ -872,6 +1105,14 @@ def main():
             "traffic": traffic,
             "mfma_util_counters": read_mfma_util(MFMA_SUMMARY, PREFILL_KERNEL_SRC,
                                                  "fwd_bf16_kernel<128, false>"),
+            # the same matrix-pipe busy cycles against the shader cycles the
+            # counters' own run measured (SQ_BUSY_CYCLES per shader array)
+            "mfma_busy_pct_of_shader_cycles": read_summary_value(
+                MFMA_SUMMARY, PREFILL_KERNEL_SRC, "fwd_bf16_kernel<128, false>",
+                "mfma_busy_pct_of_shader_cycles"),
+            "shader_clock_mhz_counters": read_summary_value(
+                MFMA_SUMMARY, PREFILL_KERNEL_SRC, "fwd_bf16_kernel<128, false>",
+                "shader_clock_mhz_from_sq_busy"),
             "kernel": "fwd_bf16_kernel<128,false>",
             "flops_per_launch": head.work,
             "mean_launch_ms": round(mean_ms, 5),

@@ -180,3 +180,61 @@ def test_clock_sampler_keeps_distinct_loaded_tables(monkeypatch):
     assert reads[6][1] == (1802 + 1702) / 2 and reads[6][2] == 1202
     keys = {r[0] for r in reads[6:]}
     assert len(keys) == 2  # tables 2 and 3, three reads each
+
+
+def test_sweep_summary_splits_blocks_and_recovers_the_fit(tmp_path):
+    # synthetic trace: each shape's launches take steps*t + items*x + c
+    # microseconds in its timed window and a different time elsewhere (the
+    # settle and clock phases), with an unrelated kernel interleaved
+    t, x, c = 1.75, 3.0, 9.0
+    kt = tmp_path / "kt"
+    kt.mkdir()
+    lines, log = [], []
+    ts = 1000
+    for n in bench.SWEEP_N:
+        items = 4 * 16 * n // bench.SWEEP_ROWS_PER_ITEM // bench.SWEEP_WGS
+        steps = items * n // bench.SWEEP_KEYS_PER_STEP
+        want = steps * t + items * x + c
+        first, timed, launches = 7, 5, 20
+        for i in range(launches):
+            dur = want if first <= i < first + timed else want * 1.3
+            lines.append(("void fa::(anonymous namespace)::fwd_bf16_kernel<128, false>(fa::FwdArgs)",
+                          ts, ts + int(dur * 1e3)))
+            ts += int(dur * 1e3) + 500
+            lines.append(("elementwise_kernel", ts, ts + 100))
+            ts += 600
+        log.append(f"[sweep] n={n} launches={launches} timed_first={first} timed={timed} "
+                   f"event_mean_ms={want / 1e3:.5f} tflops=1.0")
+        if n == 1024:
+            log.append("[sweep] clock n=2048 mhz=1800.0 socket_w=1300 snapshots=3 error=None")
+    with open(kt / "kt_kernel_trace.csv", "w") as f:
+        f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        for name, a, b in reversed(lines):   # the summary sorts by start time
+            f.write(f'"{name}",{a},{b}\n')
+    (tmp_path / "run.log").write_text("\n".join(log) + "\n")
+    out = tmp_path / "sweep.txt"
+    bench.sweep_summary(str(kt), str(tmp_path / "run.log"), str(out), "cmd")
+    vals = {}
+    for ln in out.read_text().splitlines():
+        k, _, v = ln.strip().partition(":")
+        vals[k] = v.strip()
+    assert abs(float(vals["t_us_per_step"]) - t) < 1e-3
+    assert abs(float(vals["x_us_per_item"]) - x) < 1e-2
+    assert abs(float(vals["c_us_per_launch"]) - c) < 1e-2
+    # the three factors multiply to the measured fraction at N = 2048
+    frac = float(vals["frac_of_2500_tflops"])
+    prod = float(vals["product"])
+    assert abs(prod - frac) < 1e-3
+    assert abs(float(vals["clock_factor (clock / 2400 MHz)"]) - 0.75) < 1e-4
+
+
+def test_sweep_summary_rejects_a_trace_that_does_not_match_the_log(tmp_path):
+    kt = tmp_path / "kt"
+    kt.mkdir()
+    with open(kt / "kt_kernel_trace.csv", "w") as f:
+        f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
+        f.write('"fa::fwd_bf16_kernel<128, false>(fa::FwdArgs)",1,2\n')
+    (tmp_path / "run.log").write_text(
+        "[sweep] n=1024 launches=3 timed_first=0 timed=1 event_mean_ms=0.1 tflops=1\n")
+    with pytest.raises(SystemExit):
+        bench.sweep_summary(str(kt), str(tmp_path / "run.log"), str(tmp_path / "o.txt"), "cmd")
