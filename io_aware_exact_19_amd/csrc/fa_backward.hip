@@ -7,20 +7,23 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id (= rowsum(P o dP)),
 //   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three kernels, no atomics (every output element has one writer):
-//  * prep: -D_i and -lse_i / scale per row, into the workspace.  They seed
-//    the dP and S accumulators, so the products come out as dP - D and
-//    S - lse / scale and the VALU needs one multiply less per element.
-//  * dkdv: one workgroup of 4 waves (one per SIMD) per (batch, head, 128
-//    keys); each wave owns 32 keys and keeps their K and V fragments in
-//    registers while 64-row tiles of Q, dO, -lse/scale, -D stream through a ring
-//    of LDS slots.  Per 32 query rows: S = Q K^T and dP = dO V^T (keys in the
-//    lane, rows in the accumulator registers), P and dS on the VALU, then
-//    dV^T += dO^T P and dK^T += Q^T dS with the tile read transposed.
+// Two kernels, no atomics (every output element has one writer), dq first:
 //  * dq: one workgroup per (batch, head, 128 query rows); each wave owns 32
 //    rows (Q and dO fragments in registers) while 64-key tiles of K and V
 //    stream through the ring: S^T = K Q^T, dP^T = V dO^T, dS^T on the VALU,
-//    then dQ^T += K^T dS^T.
+//    then dQ^T += K^T dS^T.  It also reads its rows of O in the dO fragment
+//    layout, forms D_i once the loop's first step (score products only) is
+//    issued, and writes -D_i and -lse_i / scale of each row into the
+//    workspace for the dkdv kernel.
+//  * dkdv: one workgroup of 4 waves (one per SIMD) per (batch, head, 128
+//    keys); each wave owns 32 keys and keeps their K and V fragments in
+//    registers while 64-row tiles of Q, dO, -lse/scale, -D stream through a ring
+//    of LDS slots.  -D and -lse / scale seed the dP and S accumulators, so
+//    the products come out as dP - D and S - lse / scale and the VALU needs
+//    one multiply less per element.  Per 32 query rows: S = Q K^T and
+//    dP = dO V^T (keys in the lane, rows in the accumulator registers), P and
+//    dS on the VALU, then dV^T += dO^T P and dK^T += Q^T dS with the tile
+//    read transposed.
 // Splitting dQ from dK/dV recomputes S and dP once more but needs neither
 // atomics nor an fp32 dQ buffer, and the result is bit-reproducible.
 //
@@ -287,30 +290,6 @@ template <bool B>
 using Bool = std::integral_constant<bool, B>;
 template <int I>
 using Int = std::integral_constant<int, I>;
-
-// ---------------------------------------------------------------- prep
-template <int D>
-__global__ __launch_bounds__(kBThreads) void bwd_prep_kernel(BwdArgs a) {
-  const long long idx = (long long)blockIdx.x * kBThreads + threadIdx.x;  // (b, h, i) of [B, H, n_q]
-  const long long total = (long long)a.batch * a.heads * a.seqlen_q;
-  if (idx >= total) return;
-  const int i = (int)(idx % a.seqlen_q);
-  const long long bh = idx / a.seqlen_q;
-  const int h = (int)(bh % a.heads), b = (int)(bh / a.heads);
-  const long long off = (((long long)b * a.seqlen_q + i) * a.heads + h) * D;
-  const u32x4_t* op = (const u32x4_t*)((const uint16_t*)a.o + off);
-  const u32x4_t* gp = (const u32x4_t*)((const uint16_t*)a.dout + off);
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4_t x = op[c], y = gp[c];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      s = fmaf(bf16_lo(x[j]), bf16_lo(y[j]), fmaf(bf16_hi(x[j]), bf16_hi(y[j]), s));
-  }
-  a.ws_nd[idx] = -s;
-  a.ws_nl[idx] = -a.lse[idx] / a.scale;  // +inf for a row with no key (always masked)
-}
 
 // Owner fragments: rows [r0, r0 + 32) of a [rows][heads][D] tensor (head base
 // g) as MFMA B operands, lane l32 = row, k-slots d = 16 kk + 8 h .. + 7; rows
@@ -648,11 +627,31 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   load_owner<D>(qf, (const uint16_t*)a.q + ((long long)b * n_q * H + h) * D, rs, wq0, n_q, lane);
   load_owner<D>(gf, (const uint16_t*)a.dout + ((long long)b * n_q * H + h) * D, rs, wq0, n_q, lane);
   const bool row_live = row < n_q;
+  // this lane's row of O, read in the fragment layout of dO (each half of the
+  // wave holds one half of d), for D; used after the first pipeline step
+  bf16x8_t of[D / 16];
+  load_owner<D>(of, (const uint16_t*)a.o + ((long long)b * n_q * H + h) * D, rs, wq0, n_q, lane);
+  const long long ridx = ((long long)b * H + h) * n_q + row;
+  const float nl_row = row_live ? -a.lse[ridx] / a.scale : 0.0f;
   // exp2 argument offset (-lse * log2 e) and -D of this lane's row; rows past
   // n_q get probability 0
-  const float nlc = row_live ? a.ws_nl[((long long)b * H + h) * n_q + row] * a.scale_log2
-                             : -__builtin_inff();
-  const float nd = row_live ? a.ws_nd[((long long)b * H + h) * n_q + row] : 0.0f;
+  float nlc = 0.0f, nd = 0.0f;
+  // D = sum_d dO o O of the row; -D and -lse / scale (score units; +inf for
+  // a row with no key) go into the workspace for the dkdv kernel
+  auto row_terms = [&]() {
+    float dsum = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = fmaf((float)of[kk][e], (float)gf[kk][e], dsum);
+    dsum += __shfl_xor(dsum, 32);
+    if (row_live && half == 0) {
+      a.ws_nd[ridx] = -dsum;
+      a.ws_nl[ridx] = nl_row;
+    }
+    nlc = row_live ? nl_row * a.scale_log2 : -__builtin_inff();
+    nd = row_live ? -dsum : 0.0f;
+  };
 
   f32x16_t dq[D / 32];  // dQ^T: [d][row], lane = row
 #pragma unroll
@@ -830,6 +829,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
     barrier();
     step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
+    // the first step needs no D; by now O has landed with tile 0
+    row_terms();
     step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
     for (int u = 1; u < nt; ++u) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
@@ -840,6 +841,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     step(n, y, y, y, Int<1>{}, n, DmaTile{}, 2 * nt - 1);
     step(n, y, n, n, Int<0>{}, n, DmaTile{}, 2 * nt);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    row_terms();
   }
 
   if (row_live) {
@@ -859,23 +862,17 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.batch * a.heads * a.seqlen_q;
-  const long long g0 = (rows + kBThreads - 1) / kBThreads;
   const long long g1 = (long long)a.batch * a.heads * ceil_div(a.seqlen_k, kUnit);
   const long long g2 = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, kUnit);
-  if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (g0 > 0) {
-    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)g0), dim3(kBThreads), 0, stream, a);
+  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidValue;
+  // dq first: it writes the per-row workspace values that dkdv reads
+  if (g2 > 0) {
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)g2), dim3(kBThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (g1 > 0) {
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)g1), dim3(kBThreads), 0, stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (g2 > 0) {
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)g2), dim3(kBThreads), 0, stream, a);
     return hipGetLastError();
   }
   return hipSuccess;
