@@ -72,7 +72,8 @@ VALU_SLOTS_PER_PAIR = 4.5
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_prefill.hip")
 DECODE_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_decode.hip")
 FP8_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_fp8.hip")
-BACKWARD_KERNEL_SRC = os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", "fa_backward.hip")
+BACKWARD_KERNEL_SRC = [os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", f)
+                       for f in ("fa_backward.hip", "fa_backward_dq.hip")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_mfma_util.txt")
@@ -98,10 +99,12 @@ def _local_includes(path, seen):
 
 
 def sha256(path):
-    """Digest of a kernel source together with the local headers it includes
-    (a change to a shared helper changes the compiled kernel too)."""
+    """Digest of a kernel source (or a list of them) together with the local
+    headers it includes (a change to a shared helper changes the compiled
+    kernel too)."""
     files = []
-    _local_includes(path, files)
+    for p in ([path] if isinstance(path, str) else path):
+        _local_includes(p, files)
     h = hashlib.sha256()
     for f in files:
         with open(f, "rb") as fh:
@@ -888,7 +891,8 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
                     lines.append(f"  mfma_busy_pct_of_shader_cycles: {busy:.2f}")
     src = (FP8_KERNEL_SRC if target.startswith("fp8") else
            BACKWARD_KERNEL_SRC if target.startswith("backward") else PREFILL_KERNEL_SRC)
-    lines.append(f"kernel_source: {os.path.relpath(src, ROOT)}")
+    lines.append("kernel_source: " + ", ".join(
+        os.path.relpath(p, ROOT) for p in ([src] if isinstance(src, str) else src)))
     lines.append(f"kernel_source_sha256: {sha256(src)}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
