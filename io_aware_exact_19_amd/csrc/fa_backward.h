@@ -34,14 +34,14 @@ constexpr int kLook = 4;                       // operand fragments read ahead o
 constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format
 constexpr int kFar = 1 << 28;                  // an unbounded side of a mask interval
 
-template <int D>
+template <int D, int NW = kBWaves>
 struct BTile {
   static constexpr int kCh = D / 8;                       // 16-byte chunks per row
   static constexpr int kRowB = D * 2;                     // bytes per row in LDS
   static constexpr int kBytes = kTile * kRowB;            // one tensor's tile
-  static constexpr int kLoads = kBytes / 1024 / kBWaves;  // 1 KB DMA loads per wave per tensor
+  static constexpr int kLoads = kBytes / 1024 / NW;  // 1 KB DMA loads per wave per tensor
   static constexpr int kVec = kTile * 4;                  // one fp32 value per tile row
-  static_assert(kBytes % (1024 * kBWaves) == 0, "tile must split evenly over the waves");
+  static_assert(kBytes % (1024 * NW) == 0, "tile must split evenly over the waves");
 };
 
 // The 32 rows behind a 32x32 score accumulator enter in this order, so that

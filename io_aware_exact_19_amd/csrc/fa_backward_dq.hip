@@ -10,9 +10,17 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------- dQ
-template <int D>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  using T = BTile<D>;
+// NW waves per workgroup, 32 query rows each.  Eight (two per SIMD, 256 rows
+// sharing each K/V tile) let one wave's waits be filled by the other's work;
+// the launcher takes them at d = 128 when that grid still fills every CU.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int kUnit = NW * kWaveRows;  // query rows of one workgroup
+  // operand fragments read ahead of their product: one fewer with two waves
+  // per SIMD (256 registers each), whose partner covers the LDS latency
+  constexpr int kLookQ = NW == 8 ? 2 : kLook;
+  using T = BTile<D, NW>;
   constexpr int kSlot = 2 * T::kBytes;  // K tile, V tile
   constexpr int kPer = 2 * T::kLoads;  // DMA loads per wave per tile
   constexpr int kPieces = 2;           // K group, V group
@@ -197,13 +205,13 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     };
 
     if constexpr (kN > 0) {
-      bf16x8_t fq[kLook + 1];
+      bf16x8_t fq[kLookQ + 1];
 #pragma unroll
-      for (int i = 0; i < kLook && i < kN; ++i) fq[i] = fetch(i);
+      for (int i = 0; i < kLookQ && i < kN; ++i) fq[i] = fetch(i);
 #pragma unroll
       for (int i = 0; i < kN; ++i) {
-        if (i + kLook < kN) fq[(i + kLook) % (kLook + 1)] = fetch(i + kLook);
-        product(i, fq[i % (kLook + 1)]);
+        if (i + kLookQ < kN) fq[(i + kLookQ) % (kLookQ + 1)] = fetch(i + kLookQ);
+        product(i, fq[i % (kLookQ + 1)]);
         if constexpr (kVV) {
 #pragma unroll
           for (int q = i * 32 / kN; q < (i + 1) * 32 / kN; ++q) vpiece(q);
@@ -238,9 +246,9 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
     barrier();
-    step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
-    // the first step needs no D; by now O has landed with tile 0
+    // O was requested before tile 0, so it has landed too
     row_terms();
+    step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
     step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
     for (int u = 1; u < nt; ++u) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
@@ -270,20 +278,34 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, int NW>
 hipError_t launch_bwd_dq_t(const BwdArgs& a, hipStream_t stream) {
-  const long long g = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, kUnit);
+  const long long g = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, NW * kWaveRows);
   if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (g == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)g), dim3(kBThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, NW>), dim3((unsigned)g), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t stream) {
-  if (d == 128) return launch_bwd_dq_t<128>(a, stream);
-  if (d == 64) return launch_bwd_dq_t<64>(a, stream);
+  if (d == 128) {
+    // eight waves only when their grid (one workgroup per CU) fills the chip:
+    // on smaller grids four-wave workgroups reach twice as many CUs
+    const long long g8 = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, 8 * kWaveRows);
+    const int cus = cu_count();
+    return cus > 0 && g8 >= cus ? launch_bwd_dq_t<128, 8>(a, stream)
+                                : launch_bwd_dq_t<128, 4>(a, stream);
+  }
+  if (d == 64) return launch_bwd_dq_t<64, 4>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -516,6 +516,19 @@ def test_backward_headline_shape(causal, W):
     _bwd_case(c["batch"], c["heads"], c["seqlen"], c["seqlen"], c["d"], causal, W, seed=c["seed"])
 
 
+@pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
+    (2, 64, 520, 777, True, -1),    # ragged last 256-row unit (8 rows), n_q < n_k
+    (2, 64, 900, 600, True, 100),   # n_q > n_k: rows without keys; window
+    (1, 128, 640, 640, False, 200),  # window only
+])
+def test_backward_dq_eight_waves(B, H, n_q, n_k, causal, W):
+    """At d = 128 the dQ kernel runs eight waves (256 query rows) per
+    workgroup when batch * heads * ceil(n_q / 256) reaches the CU count (256
+    here): these shapes take that variant with ragged tails and masks."""
+    assert B * H * -(-n_q // 256) >= 256
+    _bwd_case(B, H, n_q, n_k, 128, causal, W, seed=79)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
     (2, 4, 700, 700, True, -1),
