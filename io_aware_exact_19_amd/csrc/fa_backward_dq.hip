@@ -299,11 +299,14 @@ int cu_count() {
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, hipStream_t stream) {
   if (d == 128) {
     // eight waves only when their grid (one workgroup per CU) fills the chip:
-    // on smaller grids four-wave workgroups reach twice as many CUs
+    // on smaller grids four-wave workgroups reach twice as many CUs.  Under a
+    // mask the workgroups differ in length, and the longest-first order needs
+    // at least two rounds of them to even the CUs out.
     const long long g8 = (long long)a.batch * a.heads * ceil_div(a.seqlen_q, 8 * kWaveRows);
     const int cus = cu_count();
-    return cus > 0 && g8 >= cus ? launch_bwd_dq_t<128, 8>(a, stream)
-                                : launch_bwd_dq_t<128, 4>(a, stream);
+    const int rounds = (a.causal || a.window_left >= 0) ? 2 : 1;
+    return cus > 0 && g8 >= (long long)rounds * cus ? launch_bwd_dq_t<128, 8>(a, stream)
+                                                    : launch_bwd_dq_t<128, 4>(a, stream);
   }
   if (d == 64) return launch_bwd_dq_t<64, 4>(a, stream);
   return hipErrorInvalidValue;

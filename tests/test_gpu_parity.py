@@ -517,15 +517,18 @@ def test_backward_headline_shape(causal, W):
 
 
 @pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
-    (2, 64, 520, 777, True, -1),    # ragged last 256-row unit (8 rows), n_q < n_k
-    (2, 64, 900, 600, True, 100),   # n_q > n_k: rows without keys; window
-    (1, 128, 640, 640, False, 200),  # window only
+    (2, 64, 520, 777, False, -1),   # ragged last 256-row unit (8 rows), n_q < n_k
+    (4, 64, 520, 777, True, -1),    # the same under a causal mask
+    (2, 64, 1100, 600, True, 100),  # n_q > n_k: rows without keys; window
+    (2, 64, 1000, 1000, False, 200),  # window only
 ])
 def test_backward_dq_eight_waves(B, H, n_q, n_k, causal, W):
     """At d = 128 the dQ kernel runs eight waves (256 query rows) per
     workgroup when batch * heads * ceil(n_q / 256) reaches the CU count (256
-    here): these shapes take that variant with ragged tails and masks."""
-    assert B * H * -(-n_q // 256) >= 256
+    here), or twice it under a mask: these shapes take that variant with
+    ragged tails and masks."""
+    masked = causal or W >= 0
+    assert B * H * -(-n_q // 256) >= (2 if masked else 1) * 256
     _bwd_case(B, H, n_q, n_k, 128, causal, W, seed=79)
 
 
