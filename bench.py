@@ -483,10 +483,10 @@ def time_evicted(torch, w, launches=40, warmup=10, evict_bytes=1 << 30):
     return statistics.median(a.elapsed_time(b) for a, b in pairs[warmup:])
 
 
-# B4 H16 d128 bf16 non-causal prefill at these lengths: 1, 2, 4 and 8 query
-# tiles of 256 rows per workgroup of the persistent grid (256 workgroups),
-# each tile N / 64 key steps long
-SWEEP_N = (1024, 2048, 4096, 8192)
+# B4 H16 d128 bf16 non-causal prefill at these lengths: 1 to 8 query tiles
+# of 256 rows per workgroup of the persistent grid (256 workgroups), each
+# tile N / 64 key steps long
+SWEEP_N = (1024, 2048, 3072, 4096, 6144, 8192)
 SWEEP_ROWS_PER_ITEM = 256
 SWEEP_WGS = 256
 SWEEP_KEYS_PER_STEP = 64
@@ -496,11 +496,11 @@ SWEEP_MFMA_CYCLES_PER_STEP = 2 * 32 * 32
 
 
 def profile_sweep(torch, fa, inputs, configs, args):
-    """The headline shape at the lengths of SWEEP_N, one after another, each
-    settled, warmed up and timed like a bench workload; before the N = 2048
-    shape's timing, the engine clock while that shape runs back to back.
-    Logs each shape's launch count and the position of its timed launches,
-    so that a kernel trace of the run can be split by shape."""
+    """The headline shape at the lengths of SWEEP_N, one after another: for
+    each, the engine clock while it runs back to back for --clock-s seconds,
+    then settled, warmed up and timed like a bench workload.  Logs each
+    shape's clock, launch count and the position of its timed launches, so
+    that a kernel trace of the run can be split by shape."""
     for n in SWEEP_N:
         cfg = dict(configs.PREFILL_2K, seqlen=n, name=f"dense_bf16_b4_h16_n{n}_d128")
         w = make_dense(torch, fa, inputs, configs, cfg, False)
@@ -512,10 +512,8 @@ def profile_sweep(torch, fa, inputs, configs, args):
             base()
 
         w.launch = counted
-        if n == 2048:
-            mhz, watts, snaps, err = measure_clock(torch, w, args.clock_s)
-            log(f"[sweep] clock n={n} mhz={mhz} socket_w={watts} snapshots={snaps} "
-                f"error={err}")
+        mhz, watts, snaps, err = measure_clock(torch, w, args.clock_s)
+        log(f"[sweep] clock n={n} mhz={mhz} socket_w={watts} snapshots={snaps} error={err}")
         if args.settle_ms > 0:
             settle(torch, w, args.settle_ms)
         for _ in range(args.warmup):
@@ -531,12 +529,12 @@ def profile_sweep(torch, fa, inputs, configs, args):
 
 def sweep_summary(kt_dir, log_path, out_path, cmd):
     """Split the kernel trace of a ``--profile-target prefill_sweep`` run by
-    shape, take each shape's mean duration over its timed launches, and fit
-    launch time = steps * t + items * x + c (per workgroup: steps of 64 keys,
-    query tiles).  With the engine clock of the same run this splits the
-    headline's fraction of the published peak into three factors: clock /
-    2.4 GHz, the share of the launch spent in the key loop, and the matrix
-    pipe's share of a loop step's cycles."""
+    shape, take each shape's mean duration over its timed launches, turn it
+    into engine cycles with the clock sampled on that shape, and fit
+    cycles = steps * t + items * x + c (per workgroup: steps of 64 keys,
+    query tiles).  This splits the N = 2048 launch's fraction of the
+    published peak into clock / 2.4 GHz, the share of its cycles spent in the
+    key loop, and the matrix pipe's share of a loop step's cycles."""
     import numpy as np
 
     rows = []
@@ -545,14 +543,14 @@ def sweep_summary(kt_dir, log_path, out_path, cmd):
             rows.extend(r for r in csv.DictReader(f)
                         if "fwd_bf16_kernel<128, false>" in r["Kernel_Name"])
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    blocks, clock = [], None
+    blocks, clocks = [], {}
     with open(log_path) as f:
         for line in f:
             if not line.startswith("[sweep]"):
                 continue
             kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
             if line.startswith("[sweep] clock"):
-                clock = kv
+                clocks[int(kv["n"])] = kv
             else:
                 blocks.append({k: float(v) for k, v in kv.items()})
     total = sum(int(b["launches"]) for b in blocks)
@@ -567,50 +565,52 @@ def sweep_summary(kt_dir, log_path, out_path, cmd):
         pos += int(b["launches"])
         items = 4 * 16 * n // SWEEP_ROWS_PER_ITEM // SWEEP_WGS
         steps = items * n // SWEEP_KEYS_PER_STEP
-        pts.append((n, steps, items, statistics.mean(d), statistics.median(d),
-                    b["event_mean_ms"] * 1e3))
-    a = np.array([[p[1], p[2], 1.0] for p in pts])
-    y = np.array([p[3] for p in pts])
+        ck = clocks.get(n, {})
+        mhz = float(ck["mhz"]) if ck.get("mhz") not in (None, "None") else None
+        if mhz is None:
+            raise SystemExit(f"no engine clock for N = {n}: {ck.get('error')}")
+        mean = statistics.mean(d)
+        pts.append(dict(n=n, steps=steps, items=items, mean=mean, median=statistics.median(d),
+                        event=b["event_mean_ms"] * 1e3, mhz=mhz, watts=ck.get("socket_w"),
+                        cycles=mean * mhz))
+    a = np.array([[p["steps"], p["items"], 1.0] for p in pts])
+    y = np.array([p["cycles"] for p in pts])
     (t, x, c), *_ = np.linalg.lstsq(a, y, rcond=None)
     fit = a @ np.array([t, x, c])
     lines = ["# rocprofv3 kernel trace: bf16 prefill B4 H16 d128 non-causal at N = "
              + " / ".join(str(n) for n in SWEEP_N) + ", persistent grid of 256 workgroups",
              f"command: {cmd}",
-             "(per shape: the timed launches only, located by the launch counts the run logged)",
+             "(per shape: the timed launches only, located by the launch counts the run logged;",
+             " clock: amdsmi, that shape back to back for a few seconds before its timing)",
              "",
              f"{'N':>6s} {'steps/WG':>9s} {'items/WG':>9s} {'trace_mean_us':>14s} "
-             f"{'trace_median_us':>16s} {'event_mean_us':>14s} {'fit_us':>8s}"]
+             f"{'trace_median_us':>16s} {'event_mean_us':>14s} {'clock_mhz':>10s} {'socket_w':>9s} "
+             f"{'kcycles':>9s} {'fit_kcycles':>12s}"]
     for p, fv in zip(pts, fit):
-        lines.append(f"{p[0]:6d} {p[1]:9d} {p[2]:9d} {p[3]:14.2f} {p[4]:16.2f} {p[5]:14.2f} "
-                     f"{fv:8.2f}")
+        lines.append(f"{p['n']:6d} {p['steps']:9d} {p['items']:9d} {p['mean']:14.2f} "
+                     f"{p['median']:16.2f} {p['event']:14.2f} {p['mhz']:10.1f} {str(p['watts']):>9s} "
+                     f"{p['cycles'] / 1e3:9.2f} {fv / 1e3:12.2f}")
     lines += ["",
-              "least-squares fit of launch time = steps * t + items * x + c:",
-              f"  t_us_per_step: {t:.4f}",
-              f"  x_us_per_item: {x:.3f}",
-              f"  c_us_per_launch: {c:.3f}"]
-    mhz = float(clock["mhz"]) if clock and clock.get("mhz") not in (None, "None") else None
-    n2 = next(p for p in pts if p[0] == 2048)
-    loop_share = n2[1] * t / n2[3]
-    lines += [f"engine_clock_mhz (amdsmi, N = 2048 back to back): {clock.get('mhz') if clock else None}"
-              f" socket_w: {clock.get('socket_w') if clock else None}"
-              f" tables: {clock.get('snapshots') if clock else None}"]
-    frac = (4 * 128 * 4 * 16 * 2048 * 2048) / (n2[3] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+              "least-squares fit of launch cycles = steps * t + items * x + c:",
+              f"  t_cycles_per_step: {t:.0f}",
+              f"  x_cycles_per_item: {x:.0f}",
+              f"  c_cycles_per_launch: {c:.0f}",
+              f"  max_residual_pct: {100 * float(np.max(np.abs(fit - y) / y)):.2f}"]
+    n2 = next(p for p in pts if p["n"] == 2048)
+    loop_share = n2["steps"] * t / n2["cycles"]
+    occ = SWEEP_MFMA_CYCLES_PER_STEP / t
+    # 256 CUs x 4 SIMDs x 1024 FLOP per cycle at 2.4 GHz is 2516.6 TFLOP/s,
+    # published rounded down to 2500
+    rounding = 256 * 4 * 1024 * PEAK_CLOCK_MHZ * 1e6 / 1e12 / PEAK_BF16_TFLOPS
+    frac = (4 * 128 * 4 * 16 * 2048 * 2048) / (n2["mean"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
     lines += ["decomposition of the N = 2048 launch:",
               f"  frac_of_2500_tflops: {frac:.4f}",
-              f"  loop_share (steps * t / launch): {loop_share:.4f}"]
-    if mhz:
-        cyc = t * mhz
-        # 256 CUs x 4 SIMDs x 1024 FLOP per cycle at 2.4 GHz is 2516.6
-        # TFLOP/s, published rounded down to 2500
-        rounding = 256 * 4 * 1024 * PEAK_CLOCK_MHZ * 1e6 / 1e12 / PEAK_BF16_TFLOPS
-        occ = SWEEP_MFMA_CYCLES_PER_STEP / cyc
-        lines += [f"  clock_factor (clock / 2400 MHz): {mhz / PEAK_CLOCK_MHZ:.4f}",
-                  f"  cycles_per_step: {cyc:.0f}",
-                  f"  loop_mfma_occupancy ({SWEEP_MFMA_CYCLES_PER_STEP} / cycles_per_step): "
-                  f"{occ:.4f}",
-                  f"  peak_rounding (2516.6 / 2500): {rounding:.4f}",
-                  f"  product: {mhz / PEAK_CLOCK_MHZ * loop_share * occ * rounding:.4f}"]
-    lines.append(f"kernel_source_sha256: {sha256(PREFILL_KERNEL_SRC)}")
+              f"  clock_factor (clock / 2400 MHz): {n2['mhz'] / PEAK_CLOCK_MHZ:.4f}",
+              f"  loop_share (steps * t / launch cycles): {loop_share:.4f}",
+              f"  loop_mfma_occupancy ({SWEEP_MFMA_CYCLES_PER_STEP} / t): {occ:.4f}",
+              f"  peak_rounding (2516.6 / 2500): {rounding:.4f}",
+              f"  product: {n2['mhz'] / PEAK_CLOCK_MHZ * loop_share * occ * rounding:.4f}",
+              f"kernel_source_sha256: {sha256(PREFILL_KERNEL_SRC)}"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -183,10 +183,12 @@ def test_clock_sampler_keeps_distinct_loaded_tables(monkeypatch):
 
 
 def test_sweep_summary_splits_blocks_and_recovers_the_fit(tmp_path):
-    # synthetic trace: each shape's launches take steps*t + items*x + c
-    # microseconds in its timed window and a different time elsewhere (the
-    # settle and clock phases), with an unrelated kernel interleaved
-    t, x, c = 1.75, 3.0, 9.0
+    # synthetic trace: each shape's launches take (steps*t + items*x + c)
+    # cycles at that shape's clock in its timed window and a different time
+    # elsewhere (the clock and settle phases), with an unrelated kernel
+    # interleaved
+    t, x, c = 3400.0, 9000.0, 15000.0
+    clock = {1024: 2000.0, 2048: 1900.0, 3072: 1880.0, 4096: 1850.0, 6144: 1820.0, 8192: 1800.0}
     kt = tmp_path / "kt"
     kt.mkdir()
     lines, log = [], []
@@ -194,19 +196,18 @@ def test_sweep_summary_splits_blocks_and_recovers_the_fit(tmp_path):
     for n in bench.SWEEP_N:
         items = 4 * 16 * n // bench.SWEEP_ROWS_PER_ITEM // bench.SWEEP_WGS
         steps = items * n // bench.SWEEP_KEYS_PER_STEP
-        want = steps * t + items * x + c
+        want = (steps * t + items * x + c) / clock[n]   # microseconds
         first, timed, launches = 7, 5, 20
         for i in range(launches):
             dur = want if first <= i < first + timed else want * 1.3
             lines.append(("void fa::(anonymous namespace)::fwd_bf16_kernel<128, false>(fa::FwdArgs)",
-                          ts, ts + int(dur * 1e3)))
+                          ts, ts + int(round(dur * 1e3))))
             ts += int(dur * 1e3) + 500
             lines.append(("elementwise_kernel", ts, ts + 100))
             ts += 600
+        log.append(f"[sweep] clock n={n} mhz={clock[n]} socket_w=1300 snapshots=3 error=None")
         log.append(f"[sweep] n={n} launches={launches} timed_first={first} timed={timed} "
                    f"event_mean_ms={want / 1e3:.5f} tflops=1.0")
-        if n == 1024:
-            log.append("[sweep] clock n=2048 mhz=1800.0 socket_w=1300 snapshots=3 error=None")
     with open(kt / "kt_kernel_trace.csv", "w") as f:
         f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
         for name, a, b in reversed(lines):   # the summary sorts by start time
@@ -218,14 +219,12 @@ def test_sweep_summary_splits_blocks_and_recovers_the_fit(tmp_path):
     for ln in out.read_text().splitlines():
         k, _, v = ln.strip().partition(":")
         vals[k] = v.strip()
-    assert abs(float(vals["t_us_per_step"]) - t) < 1e-3
-    assert abs(float(vals["x_us_per_item"]) - x) < 1e-2
-    assert abs(float(vals["c_us_per_launch"]) - c) < 1e-2
-    # the three factors multiply to the measured fraction at N = 2048
-    frac = float(vals["frac_of_2500_tflops"])
-    prod = float(vals["product"])
-    assert abs(prod - frac) < 1e-3
-    assert abs(float(vals["clock_factor (clock / 2400 MHz)"]) - 0.75) < 1e-4
+    assert abs(float(vals["t_cycles_per_step"]) - t) < 2
+    assert abs(float(vals["x_cycles_per_item"]) - x) < 30
+    assert abs(float(vals["c_cycles_per_launch"]) - c) < 60
+    # the factors multiply to the measured fraction at N = 2048
+    assert abs(float(vals["product"]) - float(vals["frac_of_2500_tflops"])) < 1e-3
+    assert abs(float(vals["clock_factor (clock / 2400 MHz)"]) - 1900 / 2400) < 1e-4
 
 
 def test_sweep_summary_rejects_a_trace_that_does_not_match_the_log(tmp_path):
