@@ -838,13 +838,14 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
 
     Clock: the SQ counters come back summed over the shader arrays, and
     SQ_BUSY_CYCLES / arrays / dispatch time is the shader clock the kernel
-    ran at (it agrees with the GPU metrics table's engine clock, ~1.8 GHz
-    under the prefill kernels); GRBM_GUI_ACTIVE / XCDs / dispatch time reads
-    ~2.05 GHz, so GRBM_GUI_ACTIVE does not tick at the shader clock, and the
-    derived MfmaUtil, which divides by it, understates the matrix pipes'
-    busy share.  The summary therefore also reports that share against
-    shader cycles: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x SQ_BUSY_CYCLES /
-    arrays)."""
+    ran at (a lower bound: an array stops counting once its XCD has
+    drained).  GRBM_GUI_ACTIVE spans the profiler's sampling window around
+    the dispatch (11-28 us more than the dispatch at the shader clock,
+    whatever the kernel's length), so GRBM_GUI_ACTIVE / XCDs / dispatch time
+    overstates the clock and the derived MfmaUtil, which divides by it,
+    understates the matrix pipes' busy share.  The summary therefore also
+    reports that share against shader cycles: SQ_VALU_MFMA_BUSY_CYCLES /
+    (SIMDs x SQ_BUSY_CYCLES / arrays)."""
     util = {}
     for r in _pmc_rows(util_dir):
         if r.get("Counter_Name") == "MfmaUtil" and "fa::" in r.get("Kernel_Name", ""):
@@ -889,6 +890,105 @@ def mfma_summary(util_dir, raw_dir, target, out_path, cmd, algo_flops):
                 if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
                     busy = 100.0 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * shader_cycles)
                     lines.append(f"  mfma_busy_pct_of_shader_cycles: {busy:.2f}")
+    src = (FP8_KERNEL_SRC if target.startswith("fp8") else
+           BACKWARD_KERNEL_SRC if target.startswith("backward") else PREFILL_KERNEL_SRC)
+    lines.append("kernel_source: " + ", ".join(
+        os.path.relpath(p, ROOT) for p in ([src] if isinstance(src, str) else src)))
+    lines.append(f"kernel_source_sha256: {sha256(src)}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+ANATOMY_PASSES = (
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC"),
+    ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS",
+     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_SMEM", "SQ_BUSY_CYCLES"),
+    ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_BRANCH", "SQ_BUSY_CYCLES"),
+)
+
+
+def anatomy_summary(dirs, target, out_path, cmd):
+    """Where each library kernel's waves spend their time, from three
+    rocprofv3 --pmc passes (ANATOMY_PASSES), medians per dispatch.
+
+    The SQ counters come back summed over the shader arrays; the wave-state
+    ones (SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_*) count in units of four
+    cycles, which the file checks: SQ_WAVE_CYCLES x 4 / (waves x shader
+    cycles) is the waves' residency, at most 1.  Each pass is normalised by
+    its own SQ_BUSY_CYCLES (shader cycles = SQ_BUSY_CYCLES / arrays)."""
+    med, grid = {}, {}
+    for i, d in enumerate(dirs):
+        vals = {}
+        for r in _pmc_rows(d):
+            n = r.get("Kernel_Name", "")
+            if "fa::" not in n:
+                continue
+            k = _kernel_short(n)
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+            if r.get("Grid_Size"):
+                grid[k] = int(r["Grid_Size"])
+        for k, cs in vals.items():
+            for c, v in cs.items():
+                med.setdefault(k, {})[(i, c)] = statistics.median(v)
+    arrays, simds = _agent_info(dirs[0])
+    lines = [f"# Wave-state anatomy of the {target} workload's kernels from three rocprofv3 --pmc passes",
+             f"command: {cmd}",
+             "(medians over the dispatches of each kernel; wave-state counters in units of 4 cycles)"]
+    for k in sorted(med):
+        m = med[k]
+
+        def get(c, i=None):
+            for j in ([i] if i is not None else range(len(dirs))):
+                if (j, c) in m:
+                    return m[(j, c)], j
+            return None, None
+
+        lines.append(f"kernel: {k}")
+        waves = grid.get(k, 0) // 64
+        lines.append(f"  waves: {waves}")
+        for i, names in enumerate(ANATOMY_PASSES):
+            for c in names:
+                v = m.get((i, c))
+                if v is not None:
+                    lines.append(f"  pass{i}.{c}: {v:.0f}")
+        if not arrays or not simds:
+            continue
+        wave, _ = get("SQ_WAVE_CYCLES", 0)
+        busy0, _ = get("SQ_BUSY_CYCLES", 0)
+        if wave and busy0 and waves:
+            sc0 = busy0 / arrays
+            lines.append(f"  wave_residency (SQ_WAVE_CYCLES x 4 / (waves x shader cycles)): "
+                         f"{4 * wave / (waves * sc0):.3f}")
+            for c, label in (("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_WAIT_ANY", "waiting_on_waitcnt"),
+                             ("SQ_WAIT_INST_ANY", "waiting_to_issue")):
+                v = m.get((0, c))
+                if v is not None:
+                    lines.append(f"  wave_time_pct.{label}: {100 * v / wave:.1f}")
+            for c, label in (("SQ_ACTIVE_INST_VALU", "vector"), ("SQ_ACTIVE_INST_LDS", "lds"),
+                             ("SQ_ACTIVE_INST_MISC", "misc")):
+                v = m.get((0, c))
+                if v is not None:
+                    lines.append(f"  simd_issue_pct.{label}: {100 * 4 * v / (simds * sc0):.1f}")
+        busy1 = m.get((1, "SQ_BUSY_CYCLES"))
+        mf = m.get((1, "SQ_INSTS_MFMA"))
+        if busy1 and mf:
+            mb = m.get((1, "SQ_VALU_MFMA_BUSY_CYCLES"))
+            if mb is not None:
+                lines.append(f"  simd_busy_pct.matrix: {100 * mb / (simds * busy1 / arrays):.1f}")
+            for c, label in (("SQ_INSTS_VALU", "vector_incl_matrix"), ("SQ_INSTS_LDS", "lds"),
+                             ("SQ_INSTS_SALU", "scalar"), ("SQ_INSTS_SMEM", "scalar_mem")):
+                v = m.get((1, c))
+                if v is not None:
+                    lines.append(f"  instructions_per_matrix_product.{label}: {v / mf:.2f}")
+        busy2 = m.get((2, "SQ_BUSY_CYCLES"))
+        lds = m.get((2, "SQ_LDS_IDX_ACTIVE"))
+        if busy2 and lds is not None:
+            cus = simds // 4
+            lines.append(f"  lds_active_pct (SQ_LDS_IDX_ACTIVE / (CUs x shader cycles)): "
+                         f"{100 * lds / (cus * busy2 / arrays):.1f}")
     src = (FP8_KERNEL_SRC if target.startswith("fp8") else
            BACKWARD_KERNEL_SRC if target.startswith("backward") else PREFILL_KERNEL_SRC)
     lines.append("kernel_source: " + ", ".join(
@@ -995,9 +1095,15 @@ def main():
     ap.add_argument("--trace-summary", nargs=2, metavar=("KT_DIR", "LOG"),
                     help="write the kernel-trace summary of a --profile-target run")
     ap.add_argument("--trace-title", default="")
+    ap.add_argument("--anatomy-summary", nargs=3, metavar=("DIR_A", "DIR_B", "DIR_C"),
+                    help="write the wave-state summary of three --pmc passes (ANATOMY_PASSES)")
     ap.add_argument("--sweep-summary", nargs=2, metavar=("KT_DIR", "LOG"),
                     help="write the length-sweep summary of a --profile-target prefill_sweep run")
     args = ap.parse_args()
+
+    if args.anatomy_summary:
+        anatomy_summary(args.anatomy_summary, args.pmc_target, args.pmc_out, args.pmc_cmd)
+        return 0
 
     if args.sweep_summary:
         sweep_summary(args.sweep_summary[0], args.sweep_summary[1], args.pmc_out, args.pmc_cmd)

@@ -56,9 +56,11 @@ __device__ __forceinline__ f32x16_t mma8(const i32x8_t& a, const i32x8_t& b, con
 // LDS position of 16-byte chunk c of K tile row r (8 chunks per 128-byte row):
 // the 16 rows one 16-lane group reads land in distinct bank groups
 __device__ __forceinline__ int k8_swz(int r) { return ((r >> 1) & 3) | ((r >> 3) & 4); }
-// V tile row r (key): the 8 rows one 16-lane transposing read covers land in
-// distinct bank groups
-__device__ __forceinline__ int v8_swz(int r) { return (r >> 1) & 3; }
+// V tile row r (key): a 32-lane transposing read covers 8 rows x 2 adjacent
+// chunks (2 db, 2 db + 1), two rows per 256-byte bank line; XOR with an even
+// value keeps each row's pair a pair, so the 4 rows of each parity land on 4
+// disjoint pairs of bank groups (XOR with 1 would map a pair onto itself)
+__device__ __forceinline__ int v8_swz(int r) { return ((r >> 1) & 3) << 1; }
 
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;

@@ -263,14 +263,23 @@ struct BfTile {
 };
 
 // K tiles: chunk c of row r at c ^ tile_swz(r).  The score product's
-// 16-lane groups read one chunk of 16 rows whose swizzles are all distinct.
+// 16-lane groups read one chunk of 16 rows, which must land on 16 distinct
+// 16-byte bank groups of a 256-byte bank line.  At d = 128 a row is one
+// bank line, so the 16 swizzles must differ; at d = 64 two rows share a
+// line (the row's parity picks its half), so the 8 rows of each parity need
+// distinct swizzles in 0..7: row bits 1..3.
+template <int D>
 __device__ __forceinline__ int tile_swz(int r) {
-  return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8);
+  if constexpr (D == 64) {
+    return (r >> 1) & 7;
+  } else {
+    return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8);
+  }
 }
 
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * (D * 2) + ((c ^ tile_swz(r)) & (D / 8 - 1)) * 16;
+  return r * (D * 2) + ((c ^ tile_swz<D>(r)) & (D / 8 - 1)) * 16;
 }
 
 // V tiles are read only through the transposing read, whose 16-lane groups
@@ -514,7 +523,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   for (int i = 0; i < T::kLoads; ++i) {
     const int slot = (i * kWaves + wave) * 64 + lane;
     const int r = slot / T::kKch;
-    const int ck = ((slot % T::kKch) ^ tile_swz(r)) & (T::kKch - 1);
+    const int ck = ((slot % T::kKch) ^ tile_swz<D>(r)) & (T::kKch - 1);
     const int cv = ((slot % T::kKch) ^ vtile_swz(r)) & (T::kKch - 1);
     kofs[i] = (uint32_t)r * row_bytes + (uint32_t)ck * 16;
     vofs[i] = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
@@ -643,7 +652,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   // (kk ^ y) in the upper bits, so fragment kk sits at k_base + ((kk << 5) ^ k_y).
   int k_base, k_y;
   {
-    const int r = pi_row(l32), sw = tile_swz(r);
+    const int r = pi_row(l32), sw = tile_swz<D>(r);
     k_base = r * D * 2 + ((half ^ sw) & 1) * 16;
     k_y = ((sw >> 1) & (D / 16 - 1)) << 5;
   }
@@ -954,7 +963,7 @@ __device__ __forceinline__ void issue_tile4(const uint16_t* kg, const uint16_t* 
     const int blk = i * 4 + wave;  // 1 KB block of the tile written by this wave
     const int slot = blk * 64 + lane;
     const int r = slot / T::kKch;
-    const int c = ((slot % T::kKch) ^ tile_swz(r)) & (T::kKch - 1);
+    const int c = ((slot % T::kKch) ^ tile_swz<D>(r)) & (T::kKch - 1);
     const int cv = ((slot % T::kKch) ^ vtile_swz(r)) & (T::kKch - 1);
     const uint32_t koff = (uint32_t)r * row_bytes + (uint32_t)c * 16;
     const uint32_t voff = (uint32_t)r * row_bytes + (uint32_t)cv * 16;
