@@ -677,9 +677,9 @@ def cpu_baseline(cfg):
 
     def add(workload, sample, seconds, work, unit):
         scale = 1e9
-        per.append(dict(workload=workload, sample=sample, seconds=round(seconds, 3),
+        per.append(dict(workload=workload, sample=sample, seconds=round(seconds, 5),
                         value=round(work / seconds / scale, 3), unit=unit))
-        log(f"[bench] oracle {workload}: {seconds:.2f} s, {work / seconds / scale:.2f} {unit}")
+        log(f"[bench] oracle {workload}: {seconds:.4f} s, {work / seconds / scale:.2f} {unit}")
 
     # small fp32 workload, whole
     c = configs.SMALL_FP32
