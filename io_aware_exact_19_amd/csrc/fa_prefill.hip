@@ -95,10 +95,44 @@ struct Work {
   long long lse_base;     // lse offset of the sequence's row 0 for head h
 };
 
+// Sequence with the r-th longest KV cache (ties: lower index first), for at
+// most 64 sequences; the same value in every lane
+__device__ __forceinline__ int kv_seq_by_rank(const FwdArgs& a, int r) {
+  const int lane = threadIdx.x & 63;
+  const int len = lane < a.batch ? min(max(a.seqlens_k[lane], 0), a.kv_rows) : -1;
+  int rank = 0;
+  for (int j = 0; j < a.batch; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(lane < a.batch && rank == r);
+  return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(m));
+}
+
+// KV: a KV-cache launch (its own kernel instantiation, so that the other
+// launches carry none of this code)
+template <bool KV>
 __device__ __forceinline__ void dense_work(const FwdArgs& a, int nqt, Work& w, int item, int n_items) {
   const int nbh = a.batch * a.heads;
-  int bh, t;  // t: rank of the tile in start order, 0 = started first
-  if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
+  int bh = 0, t = 0;  // t: rank of the tile in start order, 0 = started first
+  bool ordered = false;
+  if constexpr (KV) {
+    if ((a.causal || a.window_left >= 0) && a.heads % 8 == 0 && a.batch <= 64) {
+      // KV caches of different lengths: XCD x (workgroup i runs on XCD i %
+      // 8) takes heads x, x + 8, ... of every sequence and starts them
+      // longest cache first, the tiles of one (sequence, head) next to each
+      // other so that they run together and read its keys once through the
+      // XCD's L2
+      const int x = item & 7, k = item >> 3, upx = a.heads >> 3;
+      const int j = k / nqt;
+      t = k - j * nqt;
+      const int r = j / upx, mh = j - r * upx;
+      bh = kv_seq_by_rank(a, r) * a.heads + x + 8 * mh;
+      ordered = true;
+    }
+  }
+  if (ordered) {
+  } else if ((a.causal || a.window_left >= 0) && nbh % 8 == 0) {
     // Tiles differ in length.  Workgroup i goes to XCD i % 8, which starts
     // its workgroups in order as CUs free up: give XCD x the (batch, head)
     // units x, x + 8, x + 16, ... (a share of every sequence, which matters
@@ -432,7 +466,7 @@ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 // explicitly (vmcnt) before it, so loads of later tiles stay in flight.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool KV>
 __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   using T = BfTile<D, kThreads>;
   // ring of 4 tile slots; slot s holds K at s * 2 * kBytes and V right after
@@ -481,7 +515,7 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
       if (!varlen_work(a, kBR, lane, w)) return false;
     } else {
       if (id >= n_items) return false;
-      dense_work(a, nqt, w, id, n_items);
+      dense_work<KV>(a, nqt, w, id, n_items);
     }
     it.qg = (const uint16_t*)a.q + (w.q_row0 * a.heads + w.h) * D;
     it.kg = (const uint16_t*)a.k + (w.k_row0 * a.heads + w.h) * D;
@@ -933,9 +967,9 @@ __device__ __forceinline__ void fwd_bf16_body(const FwdArgs& a) {
   }
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool KV>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdArgs a) {
-  fwd_bf16_body<D, VARLEN>(a);
+  fwd_bf16_body<D, VARLEN, KV>(a);
 }
 
 // The four-wave kernel keeps its reference max while a lane's probabilities
@@ -973,7 +1007,7 @@ __device__ __forceinline__ void issue_tile4(const uint16_t* kg, const uint16_t* 
 }
 
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool KV>
 __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
   using T = BfTile<D, kQThreads>;
   __shared__ __attribute__((aligned(1024))) char k_lds0[T::kBytes];
@@ -989,7 +1023,7 @@ __global__ __launch_bounds__(kQThreads, 2) void fwd_bf16_q_kernel(FwdArgs a) {
   if constexpr (VARLEN) {
     if (!varlen_work(a, kQRows, lane, w)) return;
   } else {
-    dense_work(a, ceil_div(a.seqlen_q, kQRows), w, blockIdx.x, gridDim.x);
+    dense_work<KV>(a, ceil_div(a.seqlen_q, kQRows), w, blockIdx.x, gridDim.x);
   }
 
   const long long rs = (long long)a.heads * D;  // elements between consecutive rows
@@ -1232,7 +1266,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fwd_fp32_kernel(FwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
 
   Work w;
-  dense_work(a, ceil_div(a.seqlen_q, kBR32), w, blockIdx.x, gridDim.x);
+  dense_work<false>(a, ceil_div(a.seqlen_q, kBR32), w, blockIdx.x, gridDim.x);
   const long long rs = (long long)a.heads * D;
   const float* qg = (const float*)a.q + (w.q_row0 * a.heads + w.h) * D;
   const float* kg = (const float*)a.k + (w.k_row0 * a.heads + w.h) * D;
@@ -1383,8 +1417,12 @@ hipError_t launch_bf16_d128(const FwdArgs& a, hipStream_t stream) {
     const int slots = persistent_slots();
     if (slots >= 8 && grid > slots) grid = slots;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<128, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     stream, a);
+  if (!VARLEN && a.seqlens_k != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, false, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, VARLEN, false>), dim3((unsigned)grid), dim3(kThreads),
+                       0, stream, a);
   return hipGetLastError();
 }
 
@@ -1394,8 +1432,12 @@ hipError_t launch_bf16_d64(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)a.batch * a.heads * nqt;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_bf16_q_kernel<64, VARLEN>), dim3((unsigned)grid), dim3(kQThreads), 0,
-                     stream, a);
+  if (!VARLEN && a.seqlens_k != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_q_kernel<64, false, true>), dim3((unsigned)grid), dim3(kQThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_q_kernel<64, VARLEN, false>), dim3((unsigned)grid),
+                       dim3(kQThreads), 0, stream, a);
   return hipGetLastError();
 }
 

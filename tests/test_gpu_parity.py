@@ -457,6 +457,16 @@ def test_kvcache_small(d, n_new, causal, W):
     _kvcache_case(3, 4, 1100, d, [1100, 700, 300], n_new, causal, W, seed=47)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,W", [(True, -1), (True, 100), (False, 150)])
+def test_kvcache_longest_first(d, causal, W):
+    """batch * heads a multiple of 8 under a mask, heads a multiple of 8: the
+    KV-cache work order that starts sequences longest cache first (ranked in
+    the kernel, ties by index), with equal lengths, an empty cache and caches
+    shorter than the new tokens (rows without keys)."""
+    _kvcache_case(5, 8, 1100, d, [700, 1100, 0, 1100, 200], 300, causal, W, seed=53)
+
+
 def test_kvcache_queries_without_keys():
     """A sequence shorter than the chunk: its first queries see no key (O = 0, lse = -inf)."""
     _kvcache_case(2, 2, 64, 128, [3, 64], 5, True, -1, seed=48)
