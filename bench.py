@@ -77,6 +77,9 @@ BACKWARD_KERNEL_SRC = [os.path.join(ROOT, "io_aware_exact_19_amd", "csrc", f)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_hbm_traffic.txt")
 DECODE_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_bf16_b64h32_hbm_traffic.txt")
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "prefill_bf16_d128_b4h16n2048_mfma_util.txt")
+# the headline kernel as rocprofv3 names it (template arguments: head dim,
+# varlen, KV cache)
+HEADLINE_KERNEL = "fwd_bf16_kernel<128, false, false>"
 COPY_BYTES = 512 << 20
 
 
@@ -541,7 +544,7 @@ def sweep_summary(kt_dir, log_path, out_path, cmd):
     for path in glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as f:
             rows.extend(r for r in csv.DictReader(f)
-                        if "fwd_bf16_kernel<128, false>" in r["Kernel_Name"])
+                        if HEADLINE_KERNEL in r["Kernel_Name"])
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     blocks, clocks = [], {}
     with open(log_path) as f:
@@ -1214,16 +1217,16 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "mfma_util_counters": read_mfma_util(MFMA_SUMMARY, PREFILL_KERNEL_SRC,
-                                                 "fwd_bf16_kernel<128, false>"),
+                                                 HEADLINE_KERNEL),
             # the same matrix-pipe busy cycles against the shader cycles the
             # counters' own run measured (SQ_BUSY_CYCLES per shader array)
             "mfma_busy_pct_of_shader_cycles": read_summary_value(
-                MFMA_SUMMARY, PREFILL_KERNEL_SRC, "fwd_bf16_kernel<128, false>",
+                MFMA_SUMMARY, PREFILL_KERNEL_SRC, HEADLINE_KERNEL,
                 "mfma_busy_pct_of_shader_cycles"),
             "shader_clock_mhz_counters": read_summary_value(
-                MFMA_SUMMARY, PREFILL_KERNEL_SRC, "fwd_bf16_kernel<128, false>",
+                MFMA_SUMMARY, PREFILL_KERNEL_SRC, HEADLINE_KERNEL,
                 "shader_clock_mhz_from_sq_busy"),
-            "kernel": "fwd_bf16_kernel<128,false>",
+            "kernel": HEADLINE_KERNEL,
             "flops_per_launch": head.work,
             "mean_launch_ms": round(mean_ms, 5),
             "chunk_ms_range": chunks,

@@ -200,7 +200,7 @@ def test_sweep_summary_splits_blocks_and_recovers_the_fit(tmp_path):
         first, timed, launches = 7, 5, 20
         for i in range(launches):
             dur = want if first <= i < first + timed else want * 1.3
-            lines.append(("void fa::(anonymous namespace)::fwd_bf16_kernel<128, false>(fa::FwdArgs)",
+            lines.append((f"void fa::(anonymous namespace)::{bench.HEADLINE_KERNEL}(fa::FwdArgs)",
                           ts, ts + int(round(dur * 1e3))))
             ts += int(dur * 1e3) + 500
             lines.append(("elementwise_kernel", ts, ts + 100))
@@ -232,7 +232,7 @@ def test_sweep_summary_rejects_a_trace_that_does_not_match_the_log(tmp_path):
     kt.mkdir()
     with open(kt / "kt_kernel_trace.csv", "w") as f:
         f.write('"Kernel_Name","Start_Timestamp","End_Timestamp"\n')
-        f.write('"fa::fwd_bf16_kernel<128, false>(fa::FwdArgs)",1,2\n')
+        f.write(f'"fa::{bench.HEADLINE_KERNEL}(fa::FwdArgs)",1,2\n')
     (tmp_path / "run.log").write_text(
         "[sweep] n=1024 launches=3 timed_first=0 timed=1 event_mean_ms=0.1 tflops=1\n")
     with pytest.raises(SystemExit):
