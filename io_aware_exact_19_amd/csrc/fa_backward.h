@@ -233,6 +233,15 @@ __device__ __forceinline__ void bwd_unit(int nbh, int nt, int order, int& bh, in
   }
 }
 
+// Compute units of the current device rounded down to a multiple of 8 (the
+// grid of a persistent launch, one workgroup per CU); 0 if the query fails.
+inline int bwd_slots() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n & ~7;
+}
+
 // Element masks without scalar compares: bit c of the word is set iff
 // lo <= c <= hi (c = 16 (r / 8) + r % 8 in 0..31, the row or key offset of
 // accumulator register r inside its block), and an element is kept by
@@ -254,7 +263,7 @@ __device__ __forceinline__ float keep_bit(uint32_t m, int c, float x) {
 // waits use one constant count.
 struct DmaTile {
   u32x4_t x, y, vec;
-  char* lds;
+  uint32_t lds;  // LDS byte address of the ring slot
 };
 
 template <bool B>

@@ -17,9 +17,13 @@
 //    issued, and writes -D_i and -lse_i / scale of each row into the
 //    workspace for the dkdv kernel.
 //  * dkdv: one workgroup of 4 waves (one per SIMD) per (batch, head, 128
-//    keys); each wave owns 32 keys and keeps their K and V fragments in
-//    registers while 64-row tiles of Q, dO, -lse/scale, -D stream through a ring
-//    of LDS slots.  -D and -lse / scale seed the dP and S accumulators, so
+//    keys), or at d = 128 with more such items than CUs one persistent
+//    workgroup per CU walking several of them; each wave owns 32 keys and
+//    keeps their K and V fragments in registers while 64-row tiles of Q, dO,
+//    -lse/scale, -D stream through a ring of LDS slots.  A persistent
+//    workgroup queues the next item's first two tiles in the two loads after
+//    the current item's last tile and its K, V once the current item's score
+//    products are done.  -D and -lse / scale seed the dP and S accumulators, so
 //    the products come out as dP - D and S - lse / scale and the VALU needs
 //    one multiply less per element.  Per 32 query rows: S = Q K^T and
 //    dP = dO V^T (keys in the lane, rows in the accumulator registers), P and
@@ -46,6 +50,38 @@ namespace fa {
 namespace {
 
 // ---------------------------------------------------------------- dK, dV
+// Work items: (batch, head, 128-key tile).  On small grids each workgroup
+// runs one item (bwd_unit).  Larger launches are persistent (see
+// launch_bwd_dkdv_t): one workgroup per CU, grid a multiple of 8, and XCD x
+// walks the items of the heads x, x + 8, ... in rounds, local workgroup w
+// taking item r * G8 + w of the XCD's list in even rounds and
+// r * G8 + G8 - 1 - w in odd ones.  Under a mask the list runs in rank order
+// (rank 0 = the tile with the most query rows, every head's tile of one rank
+// before the next rank), so long and short items of consecutive rounds pair
+// up; without one every item costs the same and the list is head by head,
+// so the tiles that run together share their head's Q and dO in the L2.
+__device__ __forceinline__ bool dkdv_item(int r, int nbh, int nkt, int order, int& bh, int& kt) {
+  if ((long long)gridDim.x >= (long long)nbh * nkt) {
+    if (r > 0) return false;
+    bwd_unit(nbh, nkt, order, bh, kt);
+    return true;
+  }
+  const int g8 = (int)gridDim.x >> 3, wb = (int)blockIdx.x >> 3, x = (int)blockIdx.x & 7;
+  const int hx = nbh >> 3;
+  const int k = r * g8 + ((r & 1) ? g8 - 1 - wb : wb);
+  if (k >= hx * nkt) return false;
+  if (order == 0) {
+    const int j = k / nkt;
+    bh = x + 8 * j;
+    kt = k - j * nkt;
+  } else {
+    const int rank = k / hx;
+    bh = x + 8 * (k - rank * hx);
+    kt = order < 0 ? nkt - 1 - rank : rank;
+  }
+  return true;
+}
+
 template <int D>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using T = BTile<D>;
@@ -60,40 +96,46 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int H = a.heads, n_q = a.seqlen_q, n_k = a.seqlen_k, delta = n_k - n_q;
   const int W = a.window_left;
   const bool causal = a.causal != 0;
-  const int nkt = ceil_div(n_k, kUnit);
-  int bh, kt;
-  bwd_unit(a.batch * H, nkt, causal ? 1 : (W >= 0 ? -1 : 0), bh, kt);
-  const int h = bh % H, b = bh / H;
+  const int nkt = ceil_div(n_k, kUnit), nbh = a.batch * H;
+  const int order = causal ? 1 : (W >= 0 ? -1 : 0);
   const long long rs = (long long)H * D;
   const uint32_t row_bytes = (uint32_t)(rs * 2);
-  const int k0 = kt * kUnit, wk0 = k0 + wave * kWaveRows;
-  const int key = wk0 + l32;  // this lane's key
+  const float c2 = a.scale_log2;
 
+  // one item: its (batch, head), this wave's first key, and the 64-row tiles
+  // [t_lo, t_lo + nt) of query rows that can see one of its keys
+  struct Item {
+    int b, h, wk0, t_lo, nt;
+  };
+  auto make_item = [&](int bh_, int kt_) {
+    Item it;
+    it.h = bh_ % H;
+    it.b = bh_ / H;
+    const int k0 = kt_ * kUnit;
+    it.wk0 = k0 + wave * kWaveRows;
+    int q_lo = 0, q_hi = n_q;
+    if (causal) q_lo = max(q_lo, k0 - delta);
+    if (W >= 0) q_hi = min(q_hi, k0 + kUnit - delta + W);
+    it.t_lo = q_lo / kTile;
+    it.nt = q_hi > q_lo ? ceil_div(q_hi, kTile) - it.t_lo : 0;
+    return it;
+  };
+  int r_item = 0, bh_n = 0, kt_n = 0;
+  if (!dkdv_item(0, nbh, nkt, order, bh_n, kt_n)) return;
+  Item cur = make_item(bh_n, kt_n), nxt = cur;
+  bool has_next = false;
+  int gbase = 0;  // ring index of the current item's first tile
+
+  // K, V of this wave's 32 keys as B operands
+  auto owner = [&](const Item& it, bf16x8_t (&kx)[D / 16], bf16x8_t (&vx)[D / 16]) {
+    const long long base = ((long long)it.b * n_k * H + it.h) * D;
+    load_owner<D>(kx, (const uint16_t*)a.k + base, rs, it.wk0, n_k, lane);
+    load_owner<D>(vx, (const uint16_t*)a.v + base, rs, it.wk0, n_k, lane);
+  };
   bf16x8_t kf[D / 16], vf[D / 16];
-  load_owner<D>(kf, (const uint16_t*)a.k + ((long long)b * n_k * H + h) * D, rs, wk0, n_k, lane);
-  load_owner<D>(vf, (const uint16_t*)a.v + ((long long)b * n_k * H + h) * D, rs, wk0, n_k, lane);
+  owner(cur, kf, vf);
 
   f32x16_t dk[D / 32], dv[D / 32];  // dK^T, dV^T: [d][key], lane = key
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.0f;
-      dv[db][r] = 0.0f;
-    }
-
-  // query rows that can see one of the workgroup's keys, in 64-row tiles
-  int q_lo = 0, q_hi = n_q;
-  if (causal) q_lo = max(q_lo, k0 - delta);
-  if (W >= 0) q_hi = min(q_hi, k0 + kUnit - delta + W);
-  const int t_lo = q_lo / kTile;
-  const int nt = q_hi > q_lo ? ceil_div(q_hi, kTile) - t_lo : 0;
-
-  const uint16_t* qg = (const uint16_t*)a.q + ((long long)b * n_q * H + h) * D;
-  const uint16_t* gg = (const uint16_t*)a.dout + ((long long)b * n_q * H + h) * D;
-  const float* nlg = a.ws_nl + ((long long)b * H + h) * n_q;
-  const float* ndg = a.ws_nd + ((long long)b * H + h) * n_q;
-  const float c2 = a.scale_log2;
 
   // DMA: wave w moves the 1 KB blocks 4w .. 4w + 3 of each tensor's tile;
   // lane l of block blk fills LDS position blk * 64 + l (row r, chunk slot p)
@@ -116,34 +158,48 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       dma_b128(rsrc, xofs[1] + 1024, lds_base + 1024);
     }
   };
-  auto slot = [&](int u) { return ring + (u & (kRing - 1)) * kSlot; };
-  auto dma_setup = [&](int u) {
+  auto slot = [&](int g) { return ring + (g & (kRing - 1)) * kSlot; };
+  // the ring's LDS byte address as an integer: the DMA destinations are
+  // computed from it, without casting a slot pointer chosen at run time
+  const uint32_t ring_lds = lds_addr(ring);
+  // tile u of item it into ring slot g; u outside [0, it.nt) gives
+  // descriptors of size 0 (the loads write zeros into a free slot)
+  auto dma_tile = [&](const Item& it, int u, int g) {
     DmaTile t;
-    const int r0 = u < nt ? (t_lo + u) * kTile : 0;
-    const uint32_t rows = u < nt ? (uint32_t)min(kTile, n_q - r0) : 0u;
-    t.x = rsrc_of(qg + (long long)r0 * rs, rows * row_bytes);
-    t.y = rsrc_of(gg + (long long)r0 * rs, rows * row_bytes);
+    const bool live = u >= 0 && u < it.nt;
+    const int r0 = live ? (it.t_lo + u) * kTile : 0;
+    const uint32_t rows = live ? (uint32_t)min(kTile, n_q - r0) : 0u;
+    const long long qb = ((long long)it.b * n_q * H + it.h) * D + (long long)r0 * rs;
+    const long long vb = ((long long)it.b * H + it.h) * n_q + r0;
+    t.x = rsrc_of((const uint16_t*)a.q + qb, rows * row_bytes);
+    t.y = rsrc_of((const uint16_t*)a.dout + qb, rows * row_bytes);
     // waves 0, 2 load -lse/scale, waves 1, 3 load -D (the same values twice)
-    t.vec = rsrc_of((wave & 1) ? ndg + r0 : nlg + r0, rows * 4);
-    t.lds = slot(u);
+    t.vec = rsrc_of(((wave & 1) ? a.ws_nd : a.ws_nl) + vb, rows * 4);
+    t.lds = ring_lds + (uint32_t)(g & (kRing - 1)) * kSlot;
     return t;
+  };
+  // the two loads that follow the current item's last tile fetch the next
+  // item's first two tiles, so they are in LDS when that item starts
+  auto dma_setup = [&](int u) {
+    if (u < cur.nt || !has_next) return dma_tile(cur, u, gbase + u);
+    return dma_tile(nxt, u - cur.nt, gbase + u);
   };
   auto dma_piece = [&](const DmaTile& t, int k) {
     if (k < 2) {
-      dma_group(k == 0 ? t.x : t.y, lds_addr(t.lds + k * T::kBytes + wave * T::kLoads * 1024));
+      dma_group(k == 0 ? t.x : t.y, t.lds + k * T::kBytes + wave * T::kLoads * 1024);
     } else {
-      dma_b32(t.vec, (uint32_t)lane * 4, lds_addr(t.lds + 2 * T::kBytes + (wave & 1) * T::kVec));
+      dma_b32(t.vec, (uint32_t)lane * 4, t.lds + 2 * T::kBytes + (wave & 1) * T::kVec);
     }
   };
 
   const FragOffsets<D> fo(lane);
   f32x16_t sacc[2], dpacc[2];  // [block parity]: S and dP of one 32-row block
   bf16x8_t pf[2][2], sf[2][2];  // [block parity][16-row slice]: P and dS as B operands
-  auto block_row0 = [&](int j) { return (t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
+  auto block_row0 = [&](int j) { return (cur.t_lo + (j >> 1)) * kTile + kWaveRows * (j & 1); };
   auto block_masked = [&](int j) {
     const int r0 = block_row0(j);
-    return (causal && wk0 + kWaveRows - 1 > r0 + delta) ||
-           (W >= 0 && wk0 < r0 + kWaveRows - 1 + delta - W);
+    return (causal && cur.wk0 + kWaveRows - 1 > r0 + delta) ||
+           (W >= 0 && cur.wk0 < r0 + kWaveRows - 1 + delta - W);
   };
 
   // one pipeline step: the score products of block j + 1 (M1), the gradient
@@ -163,8 +219,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     constexpr int kN2 = kM2 ? 4 * (D / 32) : 0;
     constexpr int kN = kN1 + kN2;
     // block j + 1 and j - 1 have parity 1 - p: row block 1 - p of their tile
-    const char* x1 = slot((j + 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
-    const char* x2 = slot((j - 1) >> 1) + (1 - p) * kWaveRows * T::kRowB;
+    const char* x1 = slot(gbase + ((j + 1) >> 1)) + (1 - p) * kWaveRows * T::kRowB;
+    const char* x2 = slot(gbase + ((j - 1) >> 1)) + (1 - p) * kWaveRows * T::kRowB;
 
     auto fetch = [&](int i) -> bf16x8_t {
       const int o = op_index<kN1, kN2>(i);
@@ -180,7 +236,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // their rows: register r of half h is row 16 (r / 8) + 8 h + r % 8
     f32x16_t nl_init, nd_init;
     if constexpr (kM1) {
-      const char* vb = slot((j + 1) >> 1) + 2 * T::kBytes + (kWaveRows * (1 - p) + 8 * half) * 4;
+      const char* vb =
+          slot(gbase + ((j + 1) >> 1)) + 2 * T::kBytes + (kWaveRows * (1 - p) + 8 * half) * 4;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int off = (q >> 1) * 64 + (q & 1) * 16;
@@ -235,7 +292,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     // for the few blocks that cross a mask edge
     auto probs_masked = [&]() {
       // key <= row + delta and key >= row + delta - W, row = r0 + 8 h + c
-      const int w = key - delta - block_row0(j) - 8 * half;
+      const int w = cur.wk0 + l32 - delta - block_row0(j) - 8 * half;
       const uint32_t keep = mask_word(causal ? w : -kFar, W >= 0 ? w + W : kFar);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -286,60 +343,98 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  if (nt > 0) {
-    constexpr Bool<true> y{};
-    constexpr Bool<false> n{};
-    {
-      const DmaTile t0 = dma_setup(0), t1 = dma_setup(1);
-#pragma unroll
-      for (int k = 0; k < kPieces; ++k) dma_piece(t0, k);
-#pragma unroll
-      for (int k = 0; k < kPieces; ++k) dma_piece(t1, k);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));  // tile 0 has landed
-    barrier();
-    step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
-    step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
-    // iteration u: tile u lands, then P, dS of blocks 2u - 1 and 2u while the
-    // loads of tile u + 2 go out (one loop: separate loops for masked and
-    // unmasked blocks made the compiler spill the pipeline state to scratch)
-    for (int u = 1; u < nt; ++u) {
-      // tile u has landed once at most the loads of tile u + 1 are in flight
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
-      barrier();  // tile u visible; every wave is done with tile u - 2
-      step(y, y, y, y, Int<1>{}, y, dma_setup(u + 2), 2 * u - 1);
-      step(y, y, y, y, Int<0>{}, n, DmaTile{}, 2 * u);
-    }
-    step(n, y, y, y, Int<1>{}, n, DmaTile{}, 2 * nt - 1);
-    step(n, y, n, n, Int<0>{}, n, DmaTile{}, 2 * nt);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the size-0 loads of the last tiles
-  }
-
-  // lane holds d = 32 db + 8 (r/4) + 4 h + r%4 of its key
-  if (key < n_k) {
-    uint16_t* dkp = (uint16_t*)a.dk + (((long long)b * n_k + key) * H + h) * D;
-    uint16_t* dvp = (uint16_t*)a.dv + (((long long)b * n_k + key) * H + h) * D;
+  constexpr Bool<true> y{};
+  constexpr Bool<false> n{};
+  bool queued = false;  // the current item's first two tiles are already in flight
+  for (;;) {
+    has_next = dkdv_item(r_item + 1, nbh, nkt, order, bh_n, kt_n);
+    if (has_next) nxt = make_item(bh_n, kt_n);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + g4 * 8 + half * 4;
-        u32x2_t pk, pv;
-        pk[0] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 0], a.scale * dk[db][g4 * 4 + 1]);
-        pk[1] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 2], a.scale * dk[db][g4 * 4 + 3]);
-        pv[0] = pack_bf16x2(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]);
-        pv[1] = pack_bf16x2(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]);
-        *(u32x2_t*)(dkp + d) = pk;
-        *(u32x2_t*)(dvp + d) = pv;
+      for (int r = 0; r < 16; ++r) {
+        dk[db][r] = 0.0f;
+        dv[db][r] = 0.0f;
       }
+    const int nt = cur.nt;
+    if (nt > 0) {
+      if (!queued) {
+        const DmaTile t0 = dma_setup(0), t1 = dma_setup(1);
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) dma_piece(t0, k);
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) dma_piece(t1, k);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));  // tile 0 has landed
+      } else {
+        // tiles 0 and 1 were queued during the previous item, before its
+        // loads of this item's K, V and its output stores
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      barrier();
+      step(y, n, n, n, Int<1>{}, n, DmaTile{}, -1);
+      step(y, n, y, y, Int<0>{}, y, dma_setup(2), 0);
+      // iteration u: tile u lands, then P, dS of blocks 2u - 1 and 2u while the
+      // loads of tile u + 2 go out (one loop: separate loops for masked and
+      // unmasked blocks made the compiler spill the pipeline state to scratch)
+      for (int u = 1; u < nt; ++u) {
+        // tile u has landed once at most the loads of tile u + 1 are in flight
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPer));
+        barrier();  // tile u visible; every wave is done with tile u - 2
+        step(y, y, y, y, Int<1>{}, y, dma_setup(u + 2), 2 * u - 1);
+        step(y, y, y, y, Int<0>{}, n, DmaTile{}, 2 * u);
+      }
+      // the score products are done: the next item's K, V go out now,
+      // into the same registers
+      if (has_next) owner(nxt, kf, vf);
+      step(n, y, y, y, Int<1>{}, n, DmaTile{}, 2 * nt - 1);
+      step(n, y, n, n, Int<0>{}, n, DmaTile{}, 2 * nt);
+    } else {
+      // no query row sees these keys: dK = dV = 0
+      if (has_next) owner(nxt, kf, vf);
+    }
+
+    // lane holds d = 32 db + 8 (r/4) + 4 h + r%4 of its key
+    const int key = cur.wk0 + l32;
+    if (key < n_k) {
+      const long long ob = (((long long)cur.b * n_k + key) * H + cur.h) * D;
+      uint16_t* dkp = (uint16_t*)a.dk + ob;
+      uint16_t* dvp = (uint16_t*)a.dv + ob;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + half * 4;
+          u32x2_t pk, pv;
+          pk[0] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 0], a.scale * dk[db][g4 * 4 + 1]);
+          pk[1] = pack_bf16x2(a.scale * dk[db][g4 * 4 + 2], a.scale * dk[db][g4 * 4 + 3]);
+          pv[0] = pack_bf16x2(dv[db][g4 * 4 + 0], dv[db][g4 * 4 + 1]);
+          pv[1] = pack_bf16x2(dv[db][g4 * 4 + 2], dv[db][g4 * 4 + 3]);
+          *(u32x2_t*)(dkp + d) = pk;
+          *(u32x2_t*)(dvp + d) = pv;
+        }
+    }
+    if (!has_next) break;
+    // an item without tiles queued nothing for the next one
+    queued = nt > 0;
+    gbase += nt;
+    cur = nxt;
+    ++r_item;
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the size-0 loads of the last tiles
 }
 
 template <int D>
 hipError_t launch_bwd_dkdv_t(const BwdArgs& a, hipStream_t stream) {
-  const long long g = (long long)a.batch * a.heads * ceil_div(a.seqlen_k, kUnit);
+  const long long nbh = (long long)a.batch * a.heads;
+  long long g = nbh * ceil_div(a.seqlen_k, kUnit);
   if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   if (g == 0) return hipSuccess;
+  // d = 128 (one workgroup per CU): persistent when there are more items
+  // than CUs and the heads split evenly over the XCDs
+  if (D == 128 && nbh % 8 == 0) {
+    const int slots = bwd_slots();
+    if (slots >= 8 && g > slots) g = slots;
+  }
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)g), dim3(kBThreads), 0, stream, a);
   return hipGetLastError();
 }

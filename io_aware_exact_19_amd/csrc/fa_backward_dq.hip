@@ -112,11 +112,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_kernel(BwdArgs a) {
     const uint32_t rows = u < nt ? (uint32_t)min(kTile, n_k - r0) : 0u;
     t.x = rsrc_of(kg + (long long)r0 * rs, rows * row_bytes);
     t.y = rsrc_of(vg + (long long)r0 * rs, rows * row_bytes);
-    t.lds = slot(u);
+    t.lds = lds_addr(slot(u));
     return t;
   };
   auto dma_piece = [&](const DmaTile& t, int k) {
-    dma_group(k == 0 ? t.x : t.y, lds_addr(t.lds + k * T::kBytes + wave * T::kLoads * 1024));
+    dma_group(k == 0 ? t.x : t.y, t.lds + k * T::kBytes + wave * T::kLoads * 1024);
   };
 
   const FragOffsets<D> fo(lane);

@@ -542,6 +542,18 @@ def test_backward_dq_eight_waves(B, H, n_q, n_k, causal, W):
     _bwd_case(B, H, n_q, n_k, 128, causal, W, seed=79)
 
 
+@pytest.mark.parametrize("B,H,n_q,n_k,W", [
+    (2, 64, 100, 1000, 50),   # key tiles 0-5 of every head are seen by no query row
+    (1, 128, 300, 1400, 400),  # the same mixed with long items
+])
+def test_backward_persistent_empty_items(B, H, n_q, n_k, W):
+    """More (batch, head, key tile) items than CUs at d = 128: the dK/dV
+    kernel walks several items per workgroup, here with many items that no
+    query row can see (a left window far behind the queries), so an item
+    without tiles follows and precedes items with tiles."""
+    _bwd_case(B, H, n_q, n_k, 128, False, W, seed=97)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,n_q,n_k,causal,W", [
     (2, 4, 700, 700, True, -1),
