@@ -218,15 +218,11 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
     nl = ksat > 0 ? max(nt - ksat, 0) : nt;  // full-cost tiles, handed out first
     inc = wave_scan_dpp(nl);
   };
-  int total = 0, total_long = 0, total_q = 0, max_nt = 0;
+  int total = 0, total_long = 0, total_q = 0;
   for (int s0 = 0; s0 < nseq; s0 += 64) {
     load_chunk(s0);
     total_long += __builtin_amdgcn_readlane(inc, 63);
     total += __builtin_amdgcn_readlane(wave_scan_dpp(nt), 63);
-    int mx = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-    max_nt = max(max_nt, mx);
     if (s0 + 64 >= nseq) total_q = __builtin_amdgcn_readlane(cq1, nseq - 1 - s0);
   }
   // uniform by construction; say so, so that the work decode stays in scalar
@@ -234,7 +230,6 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
   // would be treated as divergent)
   total = __builtin_amdgcn_readfirstlane(total);
   total_long = __builtin_amdgcn_readfirstlane(total_long);
-  max_nt = __builtin_amdgcn_readfirstlane(max_nt);
   const long long live = (long long)total * a.heads;
   if ((long long)blockIdx.x >= live) return false;
   const int id = xcd_contiguous(blockIdx.x, (int)live);
@@ -257,9 +252,10 @@ __device__ bool varlen_work(const FwdArgs& a, int rows, int lane, Work& w) {
     }
   } else {
     // ramp tiles: level lvl = ksat - 1, ksat - 2, ..., 0 holds tile lvl of
-    // every sequence with more than lvl tiles, in sequence order
+    // every sequence with more than lvl tiles, in sequence order (a level no
+    // sequence reaches holds none)
     int r = g - total_long;
-    for (int lvl = min(ksat, max_nt) - 1; lvl >= 0 && src < 0; --lvl) {
+    for (int lvl = ksat - 1; lvl >= 0 && src < 0; --lvl) {
       for (int s0 = 0; s0 < nseq; s0 += 64) {
         if (nseq > 64) load_chunk(s0);  // else chunk 0 is still in registers
         unsigned long long has = __ballot(s0 + lane < nseq && nt > lvl);
